@@ -1,0 +1,245 @@
+/*
+ * msa.h -- C ABI of libmsa: MiniMax Sparse Attention (MSA) decode on AMD
+ * Instinct MI355X (CDNA4, gfx950).
+ *
+ * What the path computes [page "vLLM Adds Day-0 Support for MiniMax-M3.1-Flash
+ * on NVIDIA and AMD GPUs" (ainewsbites.com), section "A model built for
+ * efficient inference"]: the KV cache is cut into 128-token blocks; a
+ * lightweight indexer gives every key of the context a score; the scores of
+ * each block are pooled into one block score; exact attention then runs over
+ * the 16 best blocks only, the block holding the newest token always being one
+ * of them, so no query attends to more than 16 x 128 = 2,048 keys. K and V sit
+ * in an NVFP4 cache and are dequantised inside the kernels [same page, same
+ * section: the model is quantisation-aware trained for an NVFP4 KV cache;
+ * page "vLLM turns MiniMax's day-zero promise into GPU-specific serving code"
+ * (upstreambeat.ai), section "What changed": NVFP4 is dequantised inside the
+ * sparse-attention kernels].
+ *
+ * The pages define no formula for the indexer or the pooling. This library
+ * computes, for sequence b, query token t and key position j:
+ *     s[b,t,j] = sum_h w[b,t,h] * max(0, <qi[b,t,h,:], ki[j,:]>)
+ *     P[b,t,i] = max over the valid keys j of block i of s[b,t,j]
+ * and selects the top_k blocks by (P desc, block index asc) after setting the
+ * pooled score of the block holding the newest key to +inf (keep-last rule).
+ *
+ * ------------------------------------------------------------------------
+ * Conventions shared by every entry point
+ * ------------------------------------------------------------------------
+ * Ownership.  Every buffer is allocated and freed by the caller. The library
+ *   keeps no pointer after a call returns and never allocates device memory;
+ *   scratch memory comes only from the caller's workspace argument.
+ * Pointers.  Pointers named "device" must point to device memory of the
+ *   current HIP device. msa_params_t and msa_cache_t themselves are host
+ *   structures read during the call only.
+ * Execution.  Kernels are enqueued on `stream` (a hipStream_t passed as void*,
+ *   NULL = the null stream); calls return without synchronising. Outputs are
+ *   written completely (padding included). Inputs and outputs must not alias.
+ * Errors.  Argument errors that the host can see are reported before anything
+ *   is enqueued (MSA_ERR_INVALID_ARG / MSA_ERR_UNSUPPORTED / MSA_ERR_WORKSPACE);
+ *   a failed launch reports MSA_ERR_HIP. msa_last_error() returns a
+ *   thread-local text describing the last failure. Nothing aborts and no C++
+ *   exception crosses the ABI.
+ * Device data.  Values inside device buffers are not validated on the host.
+ *   The kernels never access memory through them out of bounds: a context
+ *   length above max_blocks_per_seq*128 is clamped to it, a block-table entry
+ *   outside [0, num_pages) makes that block absent (its keys get score -inf
+ *   and it is never attended), and a query token whose position p_t is
+ *   negative (ctx_lens[b] < q_len) attends to nothing (output 0, lse -inf,
+ *   no block selected).
+ *
+ * Positions.  ctx_lens[b] = L_b counts the q_len new tokens, whose K/V and
+ *   indexer keys are already in the cache. Query token t (0-based) of
+ *   sequence b sits at position p_t = L_b - q_len + t and sees keys 0..p_t
+ *   (causal inside the window of new tokens).
+ *
+ * ------------------------------------------------------------------------
+ * Paged cache layout (one page = one 128-token block)
+ * ------------------------------------------------------------------------
+ * NVFP4 element: 4-bit E2M1 code (sign, 2 exponent bits with bias 1,
+ *   1 mantissa bit: magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6). Scale: one OCP
+ *   E4M3 (e4m3fn) byte per 16 consecutive head_dim elements of one token,
+ *   times a per-tensor fp32 scale:  x = e2m1 * e4m3 * tensor_scale.
+ *   Storage cost: 64 bytes of codes + 8 scale bytes = 72 bytes for a
+ *   128-element vector, i.e. 9/16 of FP8 -- the ratio of the 34,560 and
+ *   61,440 bytes per token quoted for the NVFP4 and FP8 caches on the
+ *   ainewsbites page, section "A model built for efficient inference".
+ *   Within a byte the element with the even index is in bits 0..3.
+ *
+ * kv_dtype == MSA_KV_NVFP4 (G = num_kv_heads, P = num_pages):
+ *   k_data  u8[P][G][128 tok][64]   byte i of token row: d = 2i (low), 2i+1
+ *   k_scale u8[P][G][128 tok][8]    scale of d in [16c, 16c+16) of that token
+ *   v_data  u8[P][G][128 d][64]     DIM-MAJOR: byte i of dim row d holds
+ *                                   tokens 2i (low nibble) and 2i+1 (high)
+ *   v_scale u8[P][G][8 c][128 tok]  scale of V[tok][16c .. 16c+16)
+ * kv_dtype == MSA_KV_BF16 (no quantisation; scales must be NULL):
+ *   k_data  bf16[P][G][128 tok][128 d]
+ *   v_data  bf16[P][G][128 d][128 tok]   (dim-major, as above)
+ * V is stored dimension-major so that the reduction of P.V (over tokens) is
+ * contiguous in memory for each lane of the matrix-core operand.
+ *
+ * idx_dtype == MSA_IDX_FP8_E4M3:
+ *   idx_k       u8[P][128 tok][64]  OCP E4M3 codes
+ *   idx_k_scale f32[P][128 tok]     key = e4m3(code) * idx_k_scale[tok]
+ * idx_dtype == MSA_IDX_BF16:
+ *   idx_k       bf16[P][128 tok][64], idx_k_scale must be NULL.
+ *
+ * block_table i32[B][max_blocks_per_seq]: logical block -> page.
+ * ctx_lens    i32[B].
+ */
+#ifndef MSA_H_
+#define MSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MSA_BLOCK_SIZE 128   /* tokens per block / page */
+#define MSA_HEAD_DIM 128     /* attention head dimension */
+#define MSA_IDX_DIM 64       /* indexer key / query dimension */
+#define MSA_MAX_TOP_K 16     /* blocks attended per query token */
+#define MSA_MAX_BLOCKS 8192  /* max_blocks_per_seq limit (1,048,576 tokens) */
+#define MSA_MAX_GROUP 16     /* num_q_heads / num_kv_heads limit */
+#define MSA_NUM_STAGES 3     /* kernels enqueued by msa_decode_layer */
+
+typedef enum {
+  MSA_OK = 0,
+  MSA_ERR_INVALID_ARG = 1, /* null pointer, negative size, inconsistent shape */
+  MSA_ERR_UNSUPPORTED = 2, /* valid but outside this build's limits */
+  MSA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required */
+  MSA_ERR_HIP = 4          /* a HIP runtime call or launch failed */
+} msa_status_t;
+
+typedef enum { MSA_KV_BF16 = 0, MSA_KV_NVFP4 = 1 } msa_kv_dtype_t;
+typedef enum { MSA_IDX_BF16 = 0, MSA_IDX_FP8_E4M3 = 1 } msa_idx_dtype_t;
+
+/* Problem description (host struct). Supported: head_dim 128, idx_dim 64,
+ * block_size 128, 1 <= top_k <= 16, keep_last in {0,1},
+ * num_q_heads % num_kv_heads == 0 with a group of at most 16 query heads,
+ * 1 <= idx_heads, and either (q_len <= 4, idx_heads <= 8) or
+ * (q_len <= 8, idx_heads <= 4); 1 <= max_blocks_per_seq <= 8192. */
+typedef struct {
+  int32_t num_seqs;           /* B */
+  int32_t q_len;              /* T_q: query tokens per sequence (same for all) */
+  int32_t num_q_heads;        /* H_q */
+  int32_t num_kv_heads;       /* H_kv */
+  int32_t head_dim;           /* must be 128 */
+  int32_t idx_heads;          /* H_i */
+  int32_t idx_dim;            /* must be 64 */
+  int32_t block_size;         /* must be 128 */
+  int32_t top_k;              /* blocks kept per query token (16 in MSA) */
+  int32_t keep_last;          /* 1: the block holding p_t is always kept */
+  int32_t max_blocks_per_seq; /* columns of block_table */
+  int32_t num_pages;          /* pages in the cache arrays */
+  float softmax_scale;        /* <= 0 selects 1/sqrt(head_dim) */
+  int32_t kv_dtype;           /* msa_kv_dtype_t */
+  int32_t idx_dtype;          /* msa_idx_dtype_t */
+} msa_params_t;
+
+/* Cache description (host struct holding device pointers; layouts above). */
+typedef struct {
+  const void* k_data;
+  const void* k_scale;        /* NULL for MSA_KV_BF16 */
+  const void* v_data;
+  const void* v_scale;        /* NULL for MSA_KV_BF16 */
+  float k_tensor_scale;       /* per-tensor fp32 scale of K (NVFP4 only) */
+  float v_tensor_scale;       /* per-tensor fp32 scale of V (NVFP4 only) */
+  const void* idx_k;
+  const float* idx_k_scale;   /* NULL for MSA_IDX_BF16 */
+  const int32_t* block_table; /* device i32[B][max_blocks_per_seq] */
+  const int32_t* ctx_lens;    /* device i32[B] */
+} msa_cache_t;
+
+/* Bytes of workspace msa_decode_layer and msa_sparse_attn_decode need for
+ * these parameters (0 if the parameters are invalid). */
+size_t msa_workspace_size(const msa_params_t* p);
+
+/* Indexer: every key of every sequence is scored against the indexer query
+ * of every query token [ainewsbites page, section "A model built for
+ * efficient inference": "scores every key in the context"].
+ *   idx_q  device bf16[B][q_len][idx_heads][64]
+ *   idx_w  device f32 [B][q_len][idx_heads]   head weights
+ *   scores device f32 [B][q_len][max_blocks_per_seq*128]: s[b,t,j] for
+ *          j <= p_t, -inf for j > p_t and for keys of absent blocks. */
+msa_status_t msa_indexer_scores(const msa_params_t* p, const msa_cache_t* cache,
+                                const void* idx_q, const float* idx_w,
+                                float* scores, void* stream);
+
+/* Pool + select [same section: one score per block, the top 16 blocks, the
+ * most recent block always kept].
+ *   ctx_lens device i32[B]
+ *   scores   device f32[B][q_len][max_blocks_per_seq*128] (as written above)
+ *   pooled   device f32[B][q_len][max_blocks_per_seq] or NULL: max of each
+ *            block's valid scores; -inf past the last block of token t.
+ *   sel      device i32[B][q_len][top_k]: selected logical block indices,
+ *            ascending, padded with -1.
+ *   nsel     device i32[B][q_len] or NULL: number of selected blocks,
+ *            min(top_k, n_blk_t) with n_blk_t = ceil((p_t+1)/128).
+ * Order: block i beats block i' if P_i > P_i', or P_i == P_i' and i < i'.
+ * With keep_last the block of p_t is ranked first. NaN scores are not
+ * supported (their rank is unspecified). */
+msa_status_t msa_pool_select_blocks(const msa_params_t* p, const int32_t* ctx_lens,
+                                    const float* scores, float* pooled, int32_t* sel,
+                                    int32_t* nsel, void* stream);
+
+/* Exact attention of every query head over the keys of the selected blocks
+ * [same section: "Main attention then runs exactly, but only over the top 16
+ * blocks"], keys j <= p_t only, K/V dequantised inside the kernel.
+ *   q     device bf16[B][q_len][num_q_heads][128]
+ *   sel   device i32[B][q_len][top_k] (as produced by msa_pool_select_blocks;
+ *         entries < 0 or >= max_blocks_per_seq are skipped)
+ *   out   device bf16[B][q_len][num_q_heads][128], RNE from fp32
+ *   lse   device f32[B][q_len][num_q_heads] or NULL: natural log of
+ *         sum_j exp(softmax_scale * <q, k_j>) over the attended keys.
+ * Query head h reads KV head h / (num_q_heads / num_kv_heads). */
+msa_status_t msa_sparse_attn_decode(const msa_params_t* p, const msa_cache_t* cache,
+                                    const void* q, const int32_t* sel, void* out,
+                                    float* lse, void* workspace, size_t ws_bytes,
+                                    void* stream);
+
+/* The whole decode step of one MSA layer: indexer + pool, select, sparse
+ * attention, in MSA_NUM_STAGES kernels on `stream`.
+ *   sel_out device i32[B][q_len][top_k] or NULL: the selection used.
+ *   lse     as in msa_sparse_attn_decode, or NULL.
+ *   workspace at least msa_workspace_size(p) bytes of device memory, 256-byte
+ *   aligned; its contents on entry do not matter. */
+msa_status_t msa_decode_layer(const msa_params_t* p, const msa_cache_t* cache,
+                              const void* q, const void* idx_q, const float* idx_w,
+                              void* out, float* lse, int32_t* sel_out,
+                              void* workspace, size_t ws_bytes, void* stream);
+
+/* msa_decode_layer with a tracing hook: when `stage_events` is not NULL it
+ * holds MSA_NUM_STAGES + 1 hipEvent_t handles (created by the caller); event
+ * i is recorded on `stream` before stage i is enqueued and the last one after
+ * the last stage, so the caller can time each kernel with hipEventElapsedTime. */
+msa_status_t msa_decode_layer_traced(const msa_params_t* p, const msa_cache_t* cache,
+                                     const void* q, const void* idx_q, const float* idx_w,
+                                     void* out, float* lse, int32_t* sel_out,
+                                     void* workspace, size_t ws_bytes, void* stream,
+                                     void* const* stage_events);
+
+/* Debug exports: run the kernels' own dequantisation helpers over a flat
+ * buffer, for bit-exact tests of the decoders.
+ *   msa_debug_dequant_nvfp4: codes device u8[n_groups*8] (16 elements per
+ *   group, even element in the low nibble), scales device u8[n_groups] (E4M3),
+ *   out device f32[n_groups*16] = e2m1 * e4m3 (the tensor scale is not
+ *   applied; the kernels apply it to the dot products).
+ *   msa_debug_dequant_fp8: codes device u8[n], out device f32[n] = e4m3. */
+msa_status_t msa_debug_dequant_nvfp4(const uint8_t* codes, const uint8_t* scales,
+                                     int64_t n_groups, float* out, void* stream);
+msa_status_t msa_debug_dequant_fp8(const uint8_t* codes, int64_t n, float* out,
+                                   void* stream);
+
+/* Human-readable name of a status code (static string). */
+const char* msa_status_string(msa_status_t s);
+/* Thread-local description of the last failure in this thread ("" if none). */
+const char* msa_last_error(void);
+/* Library version string. */
+const char* msa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MSA_H_ */

@@ -1,0 +1,251 @@
+"""Benchmark of one MSA decode layer step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 3]
+
+A step is one call of msa_decode_layer (indexer + pool, select, sparse
+attention) over one batch of the chosen synthetic configuration, inputs
+resident in HBM. Consecutive steps rotate over R device replicas of the
+inputs so that no step finds its bytes in the 256 MB Infinity Cache. Prints
+one JSON line on stdout (details on stderr):
+
+  value        decode tokens/s per layer = B * T_q / step time
+  roofline     the dominant kernel (the indexer scan): algorithmic bytes per
+               launch / its average duration (HIP events on the launch
+               stream), against the 8 TB/s HBM peak
+  cpu_baseline the float64 oracle on a bounded sample of the same workload,
+               timed on this host's cores
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "MSA decode tokens/s per layer at 128K ctx; achieved HBM GB/s vs 8 TB/s peak"
+ROOT = os.path.dirname(os.path.abspath(__file__))
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------ byte models
+
+def indexer_bytes(w):
+    """Algorithmic bytes of the indexer + pool launch: every visible indexer
+    key (64 B codes + 4 B scale for FP8, 128 B for bf16), indexer queries and
+    weights, block-table entries read, pooled scores written."""
+    prm = w.params
+    B, Tq, Hi, maxb = prm["num_seqs"], prm["q_len"], prm["idx_heads"], prm["max_blocks_per_seq"]
+    L = np.minimum(w.ctx_lens.astype(np.int64), maxb * 128)
+    nblk = (L + 127) // 128
+    per_tok = 68 if prm["idx_dtype"] == 1 else 128
+    return int(L.sum() * per_tok + B * Tq * Hi * (64 * 2 + 4) + nblk.sum() * 4 + Tq * nblk.sum() * 4)
+
+
+def attention_bytes(w, sel):
+    """Algorithmic bytes of the attention launch: K+V of the union of the
+    selected blocks per (sequence, KV head) -- 144 B per token per KV head
+    for NVFP4 (codes + scales of K and V), 512 B for bf16 -- plus queries,
+    selections and bf16 outputs."""
+    prm = w.params
+    B, Tq, Hq, G = prm["num_seqs"], prm["q_len"], prm["num_q_heads"], prm["num_kv_heads"]
+    per_tok = 144 if prm["kv_dtype"] == 1 else 512
+    blocks = 0
+    for b in range(B):
+        blocks += len(set(int(x) for x in sel[b].ravel() if x >= 0))
+    return int(blocks * G * 128 * per_tok + B * Tq * Hq * 128 * 2 * 2 + B * Tq * prm["top_k"] * 4)
+
+
+# ------------------------------------------------------------ cpu baseline
+
+def cpu_baseline(w, gpu_res, budget_s=20.0):
+    """Time the oracle (as it stands) on whole sequences of the workload until
+    about budget_s seconds of CPU work; also compare its results with the GPU
+    step's on those sequences."""
+    from oracle import msa_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    prm = w.params
+    order = list(range(prm["num_seqs"]))
+    t0 = time.perf_counter()
+    done_tok, seqs, ties, max_err, max_ulp = 0, [], 0, 0.0, 0.0
+    for b in order:
+        res = O.decode_sequence(w, b)
+        done_tok += len(res)
+        seqs.append(b)
+        for t, r in enumerate(res):
+            if r["p"] < 0:
+                continue
+            g = sorted(int(x) for x in gpu_res["sel"][b, t] if x >= 0)
+            if g != list(r["sel"]):
+                ties += 1
+            else:
+                err = np.abs(gpu_res["out"][b, t] - r["out"])
+                small = np.abs(r["out"]) < 0.5
+                if small.any():
+                    max_err = max(max_err, float(err[small].max()))
+                ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(r["out"]), 2.0 ** -126))) - 7)
+                max_ulp = max(max_ulp, float(np.max(err / ulp)))
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": done_tok / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": "%d of %d sequences (%d query tokens), float64 numpy, %.1f s" % (
+                len(seqs), prm["num_seqs"], done_tok, dt),
+            "sample_check": {"tokens_with_other_selection": ties, "max_abs_where_o_below_0.5": max_err,
+                             "max_err_in_bf16_ulps": max_ulp}}
+
+
+# ------------------------------------------------------------------ main
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=3)
+    ap.add_argument("--replicas", type=int, default=0, help="input copies rotated per step (0: auto)")
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-steps", type=int, default=0,
+                    help="only run this many steps (for rocprofv3 runs); no JSON checks")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (the decode step of one "
+              "GPU's share is the unit; see DESIGN.md for how it would shard). Run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    sys.path.insert(0, ROOT)
+    import block_sparse_attention_kv_amd as msa
+    from workloads import make_config, CONFIG_NAMES
+
+    t0 = time.perf_counter()
+    w = make_config(args.config)
+    log("generated %s in %.1f s (%.2f GB host)" % (w.name, time.perf_counter() - t0, w.nbytes() / 1e9))
+    prm = w.params
+    B, Tq, Hq = prm["num_seqs"], prm["q_len"], prm["num_q_heads"]
+    step_guess = indexer_bytes(w) + B * prm["num_kv_heads"] * 64 * 128 * 144
+    R = args.replicas or max(2, min(4, int(math.ceil(3 * 256e6 / max(step_guess, 1)))))
+    dev = "cuda"
+    reps = []
+    for r in range(R):
+        params, cache, qs = msa.to_device(w, dev)
+        reps.append((params, cache, qs))
+    torch.cuda.synchronize()
+    log("uploaded %d replica(s) in %.1f s" % (R, time.perf_counter() - t0))
+    out = torch.empty((B, Tq, Hq, 128), dtype=torch.int16, device=dev)
+    lse = torch.empty((B, Tq, Hq), dtype=torch.float32, device=dev)
+    sel = torch.empty((B, Tq, prm["top_k"]), dtype=torch.int32, device=dev)
+    ws = msa.alloc_workspace(reps[0][0], dev)
+
+    def step(i, events=None):
+        params, cache, qs = reps[i % R]
+        msa.msa_decode_layer(params, cache, qs["q"], qs["idx_q"], qs["idx_w"], out, ws, lse=lse, sel_out=sel,
+                             stage_events=events)
+
+    if args.profile_steps:
+        for i in range(args.profile_steps):
+            step(i)
+        torch.cuda.synchronize()
+        log("profile run: %d steps done" % args.profile_steps)
+        # plain copy of a known size, for counter calibration
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("calibration copy: 1 GiB read + 1 GiB written")
+        return
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    gpu_res = {"sel": sel.cpu().numpy(),
+               "out": (out.view(torch.int16).cpu().numpy().astype(np.uint16).astype(np.uint32) << 16)
+               .view(np.float32).astype(np.float64)}
+
+    # ---- headline: K steps, no tracing
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record()
+    for i in range(args.steps):
+        step(i)
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = t_start.elapsed_time(t_end) / args.steps
+    log("timed %d steps: %.3f ms/step (events), %.3f ms/step (wall)" % (args.steps, ms_step, wall * 1e3 / args.steps))
+
+    # ---- per-kernel durations: the same steps with stage events
+    n_st = msa.NUM_STAGES
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_st + 1)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    stage_ms = [float(np.mean([evs[i][s].elapsed_time(evs[i][s + 1]) for i in range(args.steps)]))
+                for s in range(n_st)]
+    traced_ms = float(np.mean([evs[i][0].elapsed_time(evs[i][n_st]) for i in range(args.steps)]))
+    log("stages (ms): " + ", ".join("%s %.4f" % (n, v) for n, v in zip(msa.STAGE_NAMES, stage_ms)))
+
+    # ---- attainable copy bandwidth on this machine
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record()
+    for _ in range(10):
+        dst.copy_(src)
+    c1.record()
+    torch.cuda.synchronize()
+    copy_gbps = 2 * (1 << 30) * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    del src, dst
+
+    idx_b = indexer_bytes(w)
+    att_b = attention_bytes(w, gpu_res["sel"])
+    step_b = idx_b + att_b
+    idx_gbps = idx_b / (stage_ms[0] * 1e-3) / 1e9
+    att_gbps = att_b / (stage_ms[2] * 1e-3) / 1e9
+    step_gbps = step_b / (ms_step * 1e-3) / 1e9
+    tokens = B * Tq
+    res = {
+        "metric": METRIC,
+        "value": tokens / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16/bf16 mfma, f32 accumulate (nvfp4 K/V, fp8 idx keys in)",
+        "data": "synthetic",
+        "config": {"workload": CONFIG_NAMES[args.config], "config_id": args.config, "batch": B, "q_len": Tq,
+                   "ctx_len": int(w.ctx_lens.max()), "q_heads": Hq, "kv_heads": prm["num_kv_heads"],
+                   "idx_heads": prm["idx_heads"], "top_k": prm["top_k"], "block": 128,
+                   "input_replicas": R},
+        "roofline": {"bound": "hbm", "kernel": "indexer_pool", "achieved": idx_gbps, "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": idx_gbps / HBM_PEAK_GBPS, "traffic": None,
+                     "algorithmic_bytes": idx_b, "avg_ms": stage_ms[0]},
+        "step": {"algorithmic_bytes": step_b, "gbps": step_gbps, "frac": step_gbps / HBM_PEAK_GBPS,
+                 "stage_ms": dict(zip(msa.STAGE_NAMES, stage_ms)), "traced_ms_per_step": traced_ms,
+                 "attention_bytes": att_b, "attention_gbps": att_gbps, "copy_gbps_attainable": copy_gbps},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, gpu_res, args.cpu_budget)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

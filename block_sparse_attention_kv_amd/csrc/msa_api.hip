@@ -1,0 +1,326 @@
+// msa_api.hip -- the C ABI of libmsa (include/msa.h): host-side validation,
+// workspace carving, launch-shape choice and launches on the caller's stream.
+// No device memory is allocated here and nothing synchronises.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/msa.h"
+#include "msa_internal.hpp"
+
+using namespace msa;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+msa_status_t fail(msa_status_t s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+msa_status_t hip_fail(hipError_t e, const char* what) {
+  return fail(MSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Shape checks shared by every entry point.
+msa_status_t check_params(const msa_params_t* p) {
+  if (!p) return fail(MSA_ERR_INVALID_ARG, "params is NULL");
+  if (p->num_seqs < 1 || p->q_len < 1 || p->num_q_heads < 1 || p->num_kv_heads < 1 || p->idx_heads < 1 ||
+      p->max_blocks_per_seq < 1 || p->num_pages < 1 || p->top_k < 1)
+    return fail(MSA_ERR_INVALID_ARG, "sizes must be positive (B=%d Tq=%d Hq=%d Hkv=%d Hi=%d maxb=%d pages=%d top_k=%d)",
+                p->num_seqs, p->q_len, p->num_q_heads, p->num_kv_heads, p->idx_heads, p->max_blocks_per_seq,
+                p->num_pages, p->top_k);
+  if (p->num_q_heads % p->num_kv_heads != 0)
+    return fail(MSA_ERR_INVALID_ARG, "num_q_heads %d is not a multiple of num_kv_heads %d", p->num_q_heads,
+                p->num_kv_heads);
+  if (p->keep_last != 0 && p->keep_last != 1) return fail(MSA_ERR_INVALID_ARG, "keep_last must be 0 or 1");
+  if (p->head_dim != MSA_HEAD_DIM) return fail(MSA_ERR_UNSUPPORTED, "head_dim %d (only 128)", p->head_dim);
+  if (p->idx_dim != MSA_IDX_DIM) return fail(MSA_ERR_UNSUPPORTED, "idx_dim %d (only 64)", p->idx_dim);
+  if (p->block_size != MSA_BLOCK_SIZE) return fail(MSA_ERR_UNSUPPORTED, "block_size %d (only 128)", p->block_size);
+  if (p->top_k > MSA_MAX_TOP_K) return fail(MSA_ERR_UNSUPPORTED, "top_k %d > %d", p->top_k, MSA_MAX_TOP_K);
+  if (p->num_q_heads / p->num_kv_heads > MSA_MAX_GROUP)
+    return fail(MSA_ERR_UNSUPPORTED, "query heads per KV head %d > %d", p->num_q_heads / p->num_kv_heads,
+                MSA_MAX_GROUP);
+  if (!((p->q_len <= 4 && p->idx_heads <= 8) || (p->q_len <= 8 && p->idx_heads <= 4)))
+    return fail(MSA_ERR_UNSUPPORTED, "q_len %d with idx_heads %d (need q_len<=4 & idx_heads<=8 or q_len<=8 & idx_heads<=4)",
+                p->q_len, p->idx_heads);
+  if (p->max_blocks_per_seq > MSA_MAX_BLOCKS)
+    return fail(MSA_ERR_UNSUPPORTED, "max_blocks_per_seq %d > %d", p->max_blocks_per_seq, MSA_MAX_BLOCKS);
+  if (p->num_seqs > 65535) return fail(MSA_ERR_UNSUPPORTED, "num_seqs %d > 65535", p->num_seqs);
+  if ((int64_t)p->num_seqs * p->q_len * p->num_kv_heads > 0x7FFFFFFF)
+    return fail(MSA_ERR_UNSUPPORTED, "too many (sequence, token, head) items");
+  if (p->kv_dtype != MSA_KV_BF16 && p->kv_dtype != MSA_KV_NVFP4)
+    return fail(MSA_ERR_UNSUPPORTED, "kv_dtype %d", p->kv_dtype);
+  if (p->idx_dtype != MSA_IDX_BF16 && p->idx_dtype != MSA_IDX_FP8_E4M3)
+    return fail(MSA_ERR_UNSUPPORTED, "idx_dtype %d", p->idx_dtype);
+  if (!(p->softmax_scale == p->softmax_scale)) return fail(MSA_ERR_INVALID_ARG, "softmax_scale is NaN");
+  return MSA_OK;
+}
+
+msa_status_t check_cache_kv(const msa_params_t* p, const msa_cache_t* c) {
+  if (!c) return fail(MSA_ERR_INVALID_ARG, "cache is NULL");
+  if (!c->k_data || !c->v_data) return fail(MSA_ERR_INVALID_ARG, "k_data / v_data is NULL");
+  if (p->kv_dtype == MSA_KV_NVFP4) {
+    if (!c->k_scale || !c->v_scale) return fail(MSA_ERR_INVALID_ARG, "NVFP4 cache needs k_scale and v_scale");
+    if (!(isfinite(c->k_tensor_scale) && isfinite(c->v_tensor_scale)))
+      return fail(MSA_ERR_INVALID_ARG, "tensor scales must be finite");
+  } else if (c->k_scale || c->v_scale) {
+    return fail(MSA_ERR_INVALID_ARG, "bf16 cache takes no k_scale / v_scale");
+  }
+  if (!c->block_table || !c->ctx_lens) return fail(MSA_ERR_INVALID_ARG, "block_table / ctx_lens is NULL");
+  return MSA_OK;
+}
+
+msa_status_t check_cache_idx(const msa_params_t* p, const msa_cache_t* c) {
+  if (!c) return fail(MSA_ERR_INVALID_ARG, "cache is NULL");
+  if (!c->idx_k) return fail(MSA_ERR_INVALID_ARG, "idx_k is NULL");
+  if (p->idx_dtype == MSA_IDX_FP8_E4M3 && !c->idx_k_scale)
+    return fail(MSA_ERR_INVALID_ARG, "FP8 indexer keys need idx_k_scale");
+  if (p->idx_dtype == MSA_IDX_BF16 && c->idx_k_scale)
+    return fail(MSA_ERR_INVALID_ARG, "bf16 indexer keys take no idx_k_scale");
+  if (!c->block_table || !c->ctx_lens) return fail(MSA_ERR_INVALID_ARG, "block_table / ctx_lens is NULL");
+  return MSA_OK;
+}
+
+// Workspace of msa_decode_layer: pooled scores and the selection.
+struct Layout {
+  size_t pooled_off, sel_off, total;
+};
+Layout layout(const msa_params_t* p) {
+  Layout L;
+  const size_t bt = (size_t)p->num_seqs * p->q_len;
+  L.pooled_off = 0;
+  L.sel_off = align256(bt * p->max_blocks_per_seq * sizeof(float));
+  L.total = L.sel_off + align256(bt * p->top_k * sizeof(int32_t));
+  return L;
+}
+
+// Blocks per indexer wave: enough waves to fill 256 CUs several times over.
+int indexer_ppw(const msa_params_t* p) {
+  const int64_t blocks = (int64_t)p->num_seqs * p->max_blocks_per_seq;
+  int64_t ppw = blocks / 8192;
+  if (ppw < 1) ppw = 1;
+  if (ppw > 8) ppw = 8;
+  return (int)ppw;
+}
+
+// Waves per attention workgroup: about 2048 waves in flight, at most one
+// wave per selected block, at most 8 (16 waves of the NVFP4 kernel would
+// not fit their registers).
+int attn_waves(const msa_params_t* p) {
+  const int64_t items = (int64_t)p->num_seqs * p->q_len * p->num_kv_heads;
+  int w = 1;
+  while (w < 8 && w < p->top_k && items * w < 2048) w *= 2;
+  return w;
+}
+
+IndexerArgs indexer_args(const msa_params_t* p, const msa_cache_t* c, const void* idx_q, const float* idx_w) {
+  IndexerArgs a;
+  a.block_table = c->block_table;
+  a.ctx_lens = c->ctx_lens;
+  a.idx_k = static_cast<const uint8_t*>(c->idx_k);
+  a.idx_k_scale = c->idx_k_scale;
+  a.idx_q = static_cast<const uint16_t*>(idx_q);
+  a.idx_w = idx_w;
+  a.pooled = nullptr;
+  a.scores = nullptr;
+  a.B = p->num_seqs;
+  a.Tq = p->q_len;
+  a.Hi = p->idx_heads;
+  a.maxb = p->max_blocks_per_seq;
+  a.num_pages = p->num_pages;
+  a.ppw = indexer_ppw(p);
+  return a;
+}
+
+float softmax_scale(const msa_params_t* p) {
+  return p->softmax_scale > 0.0f ? p->softmax_scale : 1.0f / sqrtf((float)p->head_dim);
+}
+
+AttnArgs attn_args(const msa_params_t* p, const msa_cache_t* c, const void* q, const int32_t* sel, void* out,
+                   float* lse) {
+  AttnArgs a;
+  a.block_table = c->block_table;
+  a.ctx_lens = c->ctx_lens;
+  a.sel = sel;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k_data = static_cast<const uint8_t*>(c->k_data);
+  a.k_scale = static_cast<const uint8_t*>(c->k_scale);
+  a.v_data = static_cast<const uint8_t*>(c->v_data);
+  a.v_scale = static_cast<const uint8_t*>(c->v_scale);
+  a.out = static_cast<uint16_t*>(out);
+  a.lse = lse;
+  const bool fp4 = p->kv_dtype == MSA_KV_NVFP4;
+  a.score_scale = softmax_scale(p) * 1.4426950408889634f * (fp4 ? c->k_tensor_scale : 1.0f);
+  a.v_scale_mul = fp4 ? c->v_tensor_scale : 1.0f;
+  a.B = p->num_seqs;
+  a.Tq = p->q_len;
+  a.Hq = p->num_q_heads;
+  a.Hkv = p->num_kv_heads;
+  a.grp = p->num_q_heads / p->num_kv_heads;
+  a.maxb = p->max_blocks_per_seq;
+  a.num_pages = p->num_pages;
+  a.top_k = p->top_k;
+  return a;
+}
+
+void record(void* const* ev, int i, hipStream_t s) {
+  if (ev && ev[i]) (void)hipEventRecord(static_cast<hipEvent_t>(ev[i]), s);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t msa_workspace_size(const msa_params_t* p) {
+  if (check_params(p) != MSA_OK) return 0;
+  return layout(p).total;
+}
+
+msa_status_t msa_indexer_scores(const msa_params_t* p, const msa_cache_t* c, const void* idx_q, const float* idx_w,
+                                float* scores, void* stream) {
+  g_err[0] = 0;
+  msa_status_t st = check_params(p);
+  if (st != MSA_OK) return st;
+  if ((st = check_cache_idx(p, c)) != MSA_OK) return st;
+  if (!idx_q || !idx_w || !scores) return fail(MSA_ERR_INVALID_ARG, "idx_q / idx_w / scores is NULL");
+  IndexerArgs a = indexer_args(p, c, idx_q, idx_w);
+  a.scores = scores;
+  hipError_t e = launch_indexer(a, p->idx_dtype == MSA_IDX_FP8_E4M3, p->idx_heads <= 4 ? 4 : 8,
+                                static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MSA_OK : hip_fail(e, "indexer launch");
+}
+
+msa_status_t msa_pool_select_blocks(const msa_params_t* p, const int32_t* ctx_lens, const float* scores,
+                                    float* pooled, int32_t* sel, int32_t* nsel, void* stream) {
+  g_err[0] = 0;
+  msa_status_t st = check_params(p);
+  if (st != MSA_OK) return st;
+  if (!ctx_lens || !scores || !sel) return fail(MSA_ERR_INVALID_ARG, "ctx_lens / scores / sel is NULL");
+  SelectArgs a;
+  a.ctx_lens = ctx_lens;
+  a.pooled_in = nullptr;
+  a.scores_in = scores;
+  a.pooled_out = pooled;
+  a.sel = sel;
+  a.nsel = nsel;
+  a.B = p->num_seqs;
+  a.Tq = p->q_len;
+  a.maxb = p->max_blocks_per_seq;
+  a.top_k = p->top_k;
+  a.keep_last = p->keep_last;
+  hipError_t e = launch_select(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MSA_OK : hip_fail(e, "select launch");
+}
+
+msa_status_t msa_sparse_attn_decode(const msa_params_t* p, const msa_cache_t* c, const void* q, const int32_t* sel,
+                                    void* out, float* lse, void* workspace, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  (void)workspace;
+  (void)ws_bytes;
+  msa_status_t st = check_params(p);
+  if (st != MSA_OK) return st;
+  if ((st = check_cache_kv(p, c)) != MSA_OK) return st;
+  if (!q || !sel || !out) return fail(MSA_ERR_INVALID_ARG, "q / sel / out is NULL");
+  AttnArgs a = attn_args(p, c, q, sel, out, lse);
+  hipError_t e = launch_attn(a, p->kv_dtype == MSA_KV_NVFP4, attn_waves(p), static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MSA_OK : hip_fail(e, "attention launch");
+}
+
+msa_status_t msa_decode_layer_traced(const msa_params_t* p, const msa_cache_t* c, const void* q, const void* idx_q,
+                                     const float* idx_w, void* out, float* lse, int32_t* sel_out, void* workspace,
+                                     size_t ws_bytes, void* stream, void* const* ev) {
+  g_err[0] = 0;
+  msa_status_t st = check_params(p);
+  if (st != MSA_OK) return st;
+  if ((st = check_cache_kv(p, c)) != MSA_OK) return st;
+  if ((st = check_cache_idx(p, c)) != MSA_OK) return st;
+  if (!q || !idx_q || !idx_w || !out) return fail(MSA_ERR_INVALID_ARG, "q / idx_q / idx_w / out is NULL");
+  const Layout L = layout(p);
+  if (!workspace) return fail(MSA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", L.total);
+  if (ws_bytes < L.total) return fail(MSA_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, L.total);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
+    return fail(MSA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  float* pooled = reinterpret_cast<float*>(ws + L.pooled_off);
+  int32_t* sel = sel_out ? sel_out : reinterpret_cast<int32_t*>(ws + L.sel_off);
+
+  record(ev, 0, s);
+  IndexerArgs ia = indexer_args(p, c, idx_q, idx_w);
+  ia.pooled = pooled;
+  hipError_t e = launch_indexer(ia, p->idx_dtype == MSA_IDX_FP8_E4M3, p->idx_heads <= 4 ? 4 : 8, s);
+  if (e != hipSuccess) return hip_fail(e, "indexer launch");
+  record(ev, 1, s);
+
+  SelectArgs sa;
+  sa.ctx_lens = c->ctx_lens;
+  sa.pooled_in = pooled;
+  sa.scores_in = nullptr;
+  sa.pooled_out = nullptr;
+  sa.sel = sel;
+  sa.nsel = nullptr;
+  sa.B = p->num_seqs;
+  sa.Tq = p->q_len;
+  sa.maxb = p->max_blocks_per_seq;
+  sa.top_k = p->top_k;
+  sa.keep_last = p->keep_last;
+  e = launch_select(sa, s);
+  if (e != hipSuccess) return hip_fail(e, "select launch");
+  record(ev, 2, s);
+
+  AttnArgs aa = attn_args(p, c, q, sel, out, lse);
+  e = launch_attn(aa, p->kv_dtype == MSA_KV_NVFP4, attn_waves(p), s);
+  if (e != hipSuccess) return hip_fail(e, "attention launch");
+  record(ev, 3, s);
+  return MSA_OK;
+}
+
+msa_status_t msa_decode_layer(const msa_params_t* p, const msa_cache_t* c, const void* q, const void* idx_q,
+                              const float* idx_w, void* out, float* lse, int32_t* sel_out, void* workspace,
+                              size_t ws_bytes, void* stream) {
+  return msa_decode_layer_traced(p, c, q, idx_q, idx_w, out, lse, sel_out, workspace, ws_bytes, stream, nullptr);
+}
+
+msa_status_t msa_debug_dequant_nvfp4(const uint8_t* codes, const uint8_t* scales, int64_t n_groups, float* out,
+                                     void* stream) {
+  g_err[0] = 0;
+  if (n_groups < 0) return fail(MSA_ERR_INVALID_ARG, "n_groups < 0");
+  if (n_groups > 0 && (!codes || !scales || !out)) return fail(MSA_ERR_INVALID_ARG, "NULL buffer");
+  if (n_groups > (int64_t)0xFFFFFFFF * 256) return fail(MSA_ERR_UNSUPPORTED, "n_groups too large");
+  hipError_t e = launch_debug_nvfp4(codes, scales, n_groups, out, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MSA_OK : hip_fail(e, "debug launch");
+}
+
+msa_status_t msa_debug_dequant_fp8(const uint8_t* codes, int64_t n, float* out, void* stream) {
+  g_err[0] = 0;
+  if (n < 0) return fail(MSA_ERR_INVALID_ARG, "n < 0");
+  if (n > 0 && (!codes || !out)) return fail(MSA_ERR_INVALID_ARG, "NULL buffer");
+  if (n > (int64_t)0xFFFFFFFF * 2048) return fail(MSA_ERR_UNSUPPORTED, "n too large");
+  hipError_t e = launch_debug_fp8(codes, n, out, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MSA_OK : hip_fail(e, "debug launch");
+}
+
+const char* msa_status_string(msa_status_t s) {
+  switch (s) {
+    case MSA_OK: return "MSA_OK";
+    case MSA_ERR_INVALID_ARG: return "MSA_ERR_INVALID_ARG";
+    case MSA_ERR_UNSUPPORTED: return "MSA_ERR_UNSUPPORTED";
+    case MSA_ERR_WORKSPACE: return "MSA_ERR_WORKSPACE";
+    case MSA_ERR_HIP: return "MSA_ERR_HIP";
+  }
+  return "MSA_ERR_UNKNOWN";
+}
+
+const char* msa_last_error(void) { return g_err; }
+
+const char* msa_version(void) { return "libmsa 0.1 (gfx950)"; }
+
+}  // extern "C"

@@ -1,0 +1,145 @@
+"""CPU tests of the C-ABI boundary: libmsa.so loads, exports every entry point
+include/msa.h declares, and rejects bad arguments with the documented status
+before anything is launched (no GPU is touched: every call below fails host
+validation)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_sparse_attention_kv_amd as msa
+from block_sparse_attention_kv_amd import _lib
+from workloads import make_config
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _header_functions():
+    src = open(os.path.join(ROOT, "include", "msa.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(msa_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_symbols_exported():
+    L = msa.load()
+    names = _header_functions()
+    assert "msa_decode_layer" in names and len(names) >= 10
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(_lib.EXPORTED)
+
+
+def _params(**over):
+    d = dict(make_config(1).params)
+    d.update(over)
+    return msa.Params.from_dict(d)
+
+
+def _status(fn, *args):
+    st = fn(*args)
+    return st, msa.load().msa_last_error().decode()
+
+
+def _null_cache():
+    return msa.Cache()
+
+
+def test_workspace_size():
+    p = _params()
+    n = msa.msa_workspace_size(p)
+    assert n >= 4 * 1 * 1 * 32 and n % 256 == 0
+    assert msa.msa_workspace_size(_params(head_dim=64)) == 0
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(head_dim=64), _lib.MSA_ERR_UNSUPPORTED),
+    (dict(idx_dim=128), _lib.MSA_ERR_UNSUPPORTED),
+    (dict(block_size=64), _lib.MSA_ERR_UNSUPPORTED),
+    (dict(top_k=17), _lib.MSA_ERR_UNSUPPORTED),
+    (dict(top_k=0), _lib.MSA_ERR_INVALID_ARG),
+    (dict(num_q_heads=9), _lib.MSA_ERR_INVALID_ARG),
+    (dict(num_q_heads=32, num_kv_heads=1), _lib.MSA_ERR_UNSUPPORTED),
+    (dict(q_len=5, idx_heads=8), _lib.MSA_ERR_UNSUPPORTED),
+    (dict(q_len=9, idx_heads=2), _lib.MSA_ERR_UNSUPPORTED),
+    (dict(q_len=0), _lib.MSA_ERR_INVALID_ARG),
+    (dict(max_blocks_per_seq=8193), _lib.MSA_ERR_UNSUPPORTED),
+    (dict(keep_last=2), _lib.MSA_ERR_INVALID_ARG),
+    (dict(kv_dtype=7), _lib.MSA_ERR_UNSUPPORTED),
+    (dict(num_pages=0), _lib.MSA_ERR_INVALID_ARG),
+])
+def test_bad_params_rejected(over, status):
+    L = msa.load()
+    p = _params(**over)
+    c = _null_cache()
+    st, msg = _status(L.msa_decode_layer, ctypes.byref(p), ctypes.byref(c), None, None, None, None, None,
+                      None, None, 0, None)
+    assert st == status, msg
+    assert msg
+    st, msg = _status(L.msa_sparse_attn_decode, ctypes.byref(p), ctypes.byref(c), None, None, None, None,
+                      None, 0, None)
+    assert st == status, msg
+
+
+def test_null_pointers_rejected():
+    L = msa.load()
+    p = _params()
+    c = _null_cache()
+    assert L.msa_decode_layer(None, ctypes.byref(c), None, None, None, None, None, None, None, 0,
+                              None) == _lib.MSA_ERR_INVALID_ARG
+    assert L.msa_decode_layer(ctypes.byref(p), None, None, None, None, None, None, None, None, 0,
+                              None) == _lib.MSA_ERR_INVALID_ARG
+    assert L.msa_decode_layer(ctypes.byref(p), ctypes.byref(c), None, None, None, None, None, None, None, 0,
+                              None) == _lib.MSA_ERR_INVALID_ARG
+    assert "NULL" in L.msa_last_error().decode()
+    assert L.msa_indexer_scores(ctypes.byref(p), ctypes.byref(c), None, None, None, None) == \
+        _lib.MSA_ERR_INVALID_ARG
+    assert L.msa_pool_select_blocks(ctypes.byref(p), None, None, None, None, None, None) == \
+        _lib.MSA_ERR_INVALID_ARG
+    assert L.msa_debug_dequant_nvfp4(None, None, 4, None, None) == _lib.MSA_ERR_INVALID_ARG
+    assert L.msa_debug_dequant_fp8(None, -1, None, None) == _lib.MSA_ERR_INVALID_ARG
+
+
+def test_dtype_scale_consistency_rejected():
+    L = msa.load()
+    fake = ctypes.c_void_p(0x1000)
+    # bf16 KV must not carry scales; NVFP4 must
+    p = _params(kv_dtype=0, idx_dtype=0)
+    c = msa.Cache(fake, fake, fake, None, 1.0, 1.0, fake, None, fake, fake)
+    assert L.msa_sparse_attn_decode(ctypes.byref(p), ctypes.byref(c), fake, fake, fake, None, None, 0,
+                                    None) == _lib.MSA_ERR_INVALID_ARG
+    p = _params(kv_dtype=1, idx_dtype=1)
+    c = msa.Cache(fake, None, fake, fake, 1.0, 1.0, fake, None, fake, fake)
+    assert L.msa_sparse_attn_decode(ctypes.byref(p), ctypes.byref(c), fake, fake, fake, None, None, 0,
+                                    None) == _lib.MSA_ERR_INVALID_ARG
+    c = msa.Cache(fake, fake, fake, fake, 1.0, 1.0, fake, None, fake, fake)
+    assert L.msa_indexer_scores(ctypes.byref(p), ctypes.byref(c), fake, fake, fake, None) == \
+        _lib.MSA_ERR_INVALID_ARG       # FP8 keys without idx_k_scale
+
+
+def test_workspace_too_small_rejected():
+    L = msa.load()
+    fake = ctypes.c_void_p(0x1000)
+    p = _params()
+    c = msa.Cache(fake, None, fake, None, 1.0, 1.0, fake, None, fake, fake)
+    need = msa.msa_workspace_size(p)
+    assert L.msa_decode_layer(ctypes.byref(p), ctypes.byref(c), fake, fake, fake, fake, None, None, None, 0,
+                              None) == _lib.MSA_ERR_WORKSPACE
+    assert L.msa_decode_layer(ctypes.byref(p), ctypes.byref(c), fake, fake, fake, fake, None, None, fake,
+                              need - 1, None) == _lib.MSA_ERR_WORKSPACE
+    assert L.msa_decode_layer(ctypes.byref(p), ctypes.byref(c), fake, fake, fake, fake, None, None,
+                              ctypes.c_void_p(0x1010), need, None) == _lib.MSA_ERR_WORKSPACE  # misaligned
+
+
+def test_status_strings():
+    L = msa.load()
+    assert L.msa_status_string(0) == b"MSA_OK"
+    assert L.msa_status_string(3) == b"MSA_ERR_WORKSPACE"
+    assert L.msa_version().startswith(b"libmsa")
+
+
+def test_binding_raises_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        _lib.load()

@@ -1,0 +1,27 @@
+"""GPU parity at the full sizes of the large decode configurations, in the
+launch configuration bench.py times: the whole batch runs through
+msa_decode_layer, and the oracle recomputes sampled sequences one by one
+(selection tie-aware, outputs to the strict max-abs 2e-3 / mean-abs 2e-4)."""
+import numpy as np
+import pytest
+
+from tests import gpu_util as G
+from workloads import make_config
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("cfg,seqs", [(3, [0, 21]), (4, [0, 3])])
+def test_config_full_size_sampled(cfg, seqs):
+    w = make_config(cfg)
+    ties, mx, mean = G.layer_parity(w, seqs=seqs, strict=True)
+    print("cfg%d sampled %s: tie-band selections %d, out max-abs %.2e mean-abs %.2e" % (cfg, seqs, ties, mx, mean))
+
+
+def test_config5_ragged_sampled():
+    w = make_config(5)
+    order = np.argsort(w.ctx_lens)
+    seqs = sorted({int(order[0]), int(order[len(order) // 2]), int(order[-1])})
+    ties, mx, mean = G.layer_parity(w, seqs=seqs, strict=True)
+    print("cfg5 sampled %s (lens %s): tie-band selections %d, out max-abs %.2e mean-abs %.2e" % (
+        seqs, [int(w.ctx_lens[s]) for s in seqs], ties, mx, mean))

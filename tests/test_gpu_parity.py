@@ -1,0 +1,129 @@
+"""GPU parity of the HIP path (through the C ABI) against the float64 oracle.
+Tolerances are documented in tests/gpu_util.py."""
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_attention_kv_amd as msa
+from oracle import msa_oracle as O
+from tests import gpu_util as G
+from workloads import make_workload, make_config, small_cases, KV_BF16, KV_NVFP4, IDX_BF16, IDX_FP8
+
+pytestmark = pytest.mark.gpu
+
+
+def _same_bits(a, b):
+    a, b = np.asarray(a, np.float64), np.asarray(b, np.float64)
+    return bool(np.all((np.isnan(a) & np.isnan(b)) | ((a == b) & (np.signbit(a) == np.signbit(b)))))
+
+
+def test_dequant_nvfp4_bitexact():
+    # every E2M1 code through both decoders (K path: elements 0..7, V path:
+    # elements 8..15) under every E4M3 scale byte, NaN scales included
+    fwd = bytes([0x10, 0x32, 0x54, 0x76, 0x98, 0xBA, 0xDC, 0xFE])   # codes 0..15
+    rev = bytes([0xEF, 0xCD, 0xAB, 0x89, 0x67, 0x45, 0x23, 0x01])   # codes 15..0
+    codes = np.frombuffer((fwd + rev) * 256, dtype=np.uint8).copy()
+    scales = np.repeat(np.arange(256, dtype=np.uint8), 2)
+    out = torch.empty(512 * 16, dtype=torch.float32, device="cuda")
+    msa.msa_debug_dequant_nvfp4(torch.from_numpy(codes).cuda(), torch.from_numpy(scales).cuda(), out)
+    got = out.cpu().numpy().reshape(512, 16)
+    vals = O.e2m1_to_f64(O.nibbles(codes.reshape(512, 8)))
+    want = vals * O.e4m3_to_f64(scales)[:, None]
+    assert _same_bits(got, want)
+
+
+def test_dequant_fp8_bitexact():
+    codes = np.arange(256, dtype=np.uint8)
+    out = torch.empty(256, dtype=torch.float32, device="cuda")
+    msa.msa_debug_dequant_fp8(torch.from_numpy(codes).cuda(), out)
+    assert _same_bits(out.cpu().numpy(), O.e4m3_to_f64(codes))
+
+
+@pytest.mark.parametrize("idx", range(4))
+def test_indexer_scores_and_select(idx):
+    w = small_cases()[idx]
+    run = G.Run(w)
+    sc = run.scores()
+    pooled, sel, nsel = run.pool_select(sc)
+    scn = sc.cpu().numpy().astype(np.float64)
+    ref = O.decode_layer(w, want_scores=True)
+    prm = w.params
+    ties = 0
+    for b in range(prm["num_seqs"]):
+        for t in range(prm["q_len"]):
+            lab = "%s b=%d t=%d" % (w.name, b, t)
+            G.check_scores(scn[b, t], ref["scores"][b, t], lab)
+            n = int(ref["nsel"][b, t])
+            assert nsel[b, t] == n, lab
+            G.check_scores(pooled[b, t], ref["pooled"][b, t], lab + " pooled")
+            p_t = min(int(w.ctx_lens[b]), prm["max_blocks_per_seq"] * 128) - prm["q_len"] + t
+            nb = p_t // 128 + 1 if p_t >= 0 else 0
+            ties += G.check_selection(sel[b, t], ref["pooled"][b, t][:nb], ref["sel"][b, t][:n],
+                                      prm["top_k"], prm["keep_last"], lab)
+    print("%s: tie-band selection differences: %d" % (w.name, ties))
+
+
+@pytest.mark.parametrize("idx", range(4))
+def test_sparse_attention_under_oracle_selection(idx):
+    w = small_cases()[idx]
+    run = G.Run(w)
+    ref = O.decode_layer(w)
+    sel = ref["sel"].astype(np.int32)
+    out, lse = run.attend(sel)
+    mx, _, mean = G.check_out(out, ref["out"], w.name)
+    G.check_lse(lse, ref["lse"], w.name)
+    print("%s: out max-abs %.2e mean-abs %.2e" % (w.name, mx, mean))
+
+
+@pytest.mark.parametrize("idx", range(4))
+def test_decode_layer_small(idx):
+    w = small_cases()[idx]
+    ties, mx, mean = G.layer_parity(w)
+    print("%s: ties %d, out max-abs %.2e mean-abs %.2e" % (w.name, ties, mx, mean))
+
+
+def test_decode_layer_deterministic():
+    w = small_cases()[2]
+    run = G.Run(w)
+    a, b = run.layer(), run.layer()
+    assert np.array_equal(a["out_bits"], b["out_bits"])
+    assert np.array_equal(a["sel"], b["sel"])
+    assert np.array_equal(a["lse"], b["lse"])
+
+
+def test_edge_contexts():
+    # 1 token, partial blocks, exactly 16 blocks, 16 + 1 token, ctx < q_len
+    w = make_workload("edges", 31, [1, 127, 128, 129, 2047, 2048, 2049, 2176, 2], 2, 16, 2, 4,
+                      KV_NVFP4, IDX_FP8, table="permute")
+    G.layer_parity(w)
+
+
+def test_absent_pages_and_clamped_length():
+    w = make_workload("absent", 32, [3000, 5000], 1, 16, 2, 4, KV_NVFP4, IDX_FP8, table="permute")
+    w.block_table = w.block_table.copy()
+    w.block_table[0, 3] = -1
+    w.block_table[1, 7] = w.params["num_pages"] + 5
+    G.layer_parity(w)
+
+
+def test_tensor_scales_and_softmax_scale():
+    w = make_workload("scales", 33, [1000, 4000], 2, 16, 2, 4, KV_NVFP4, IDX_FP8, table="permute",
+                      k_tensor_scale=0.75, v_tensor_scale=1.5, softmax_scale=0.05)
+    G.layer_parity(w)
+
+
+def test_top_k_and_keep_last_variants():
+    for k, keep in ((4, 1), (16, 0), (1, 1)):
+        w = make_workload("k%d_keep%d" % (k, keep), 34, [3000, 700], 1, 8, 1, 3, KV_NVFP4, IDX_FP8,
+                          table="permute", top_k=k, keep_last=keep, n_planted=2)
+        G.layer_parity(w)
+
+
+def test_config1_full():
+    ties, mx, mean = G.layer_parity(make_config(1), strict=True)
+    print("cfg1: ties %d max-abs %.2e mean-abs %.2e" % (ties, mx, mean))
+
+
+def test_config2_full():
+    ties, mx, mean = G.layer_parity(make_config(2), strict=True)
+    print("cfg2: ties %d max-abs %.2e mean-abs %.2e" % (ties, mx, mean))

@@ -35,13 +35,19 @@ def hipcc():
     raise RuntimeError("hipcc not found")
 
 
+# Per-file flags. The indexer keeps matrix-core results in VGPRs (its
+# accumulators are consumed at once by vector code; the AGPR round trip costs
+# one extra instruction per element).
+FILE_FLAGS = {"indexer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
 def _compile(src, extra):
     obj = os.path.join(BUILD_DIR, os.path.basename(src)[:-4] + ".o")
-    cmd = [hipcc()] + HIPCC_FLAGS + list(extra) + ["-c", src, "-o", obj]
+    cmd = [hipcc()] + HIPCC_FLAGS + FILE_FLAGS.get(os.path.basename(src), []) + list(extra) + ["-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (src, " ".join(cmd), r.stderr))

@@ -118,6 +118,26 @@ __device__ __forceinline__ u32x4 fp8x8_f16(uint32_t lo, uint32_t hi) {
   return r;
 }
 
+// ---------------------------------------------------------------- buffers
+
+// Raw buffer resource over [base, base + bytes): loads beyond `bytes` return
+// zero without touching memory. Word 3 is the gfx9-family raw-buffer format.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// Cache policy bits of buffer loads (gfx94x/gfx950): nontemporal.
+constexpr int kAuxNT = 2;
+
+template <int AUX>
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, AUX));
+}
+template <int AUX>
+__device__ __forceinline__ float buf_load4f(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, AUX));
+}
+
 // ---------------------------------------------------------------- floats
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t h16) { return __uint_as_float(h16 << 16); }

@@ -8,23 +8,39 @@
 //     s = sum_h w[t,h] * max(0, <qi[t,h,:], k_j>),   k_j = e4m3(code) * s_tok
 // and the pooled block score is the max over the block's keys j <= p_t.
 //
-// Design. The scan reads every indexer key once, so it is HBM bound (68 bytes
-// per token for FP8 keys). One wavefront owns `ppw` consecutive blocks of one
-// sequence and streams them through the block table, prefetching the next
-// block while it computes the current one. The dot products of all T_q*H_i
-// query rows with 32 keys at a time are one 32x32x16 bf16 MFMA chain
-// (v_mfma_f32_32x32x16_bf16, 4 steps over the 64 dims): rows are query
-// vectors (t*HP + h, padded to 32), columns are keys, so every lane ends up
-// holding one key's dots for 16 query rows and the head sum, ReLU and weight
-// happen in registers. FP8 codes are widened to bf16 exactly by the hardware
-// converter; the per-token scale multiplies the dot before the ReLU.
+// Work split. The scan reads every indexer key once, so it is HBM bound (68
+// bytes per token for FP8 keys). The grid is persistent (as many workgroups
+// as fit on the chip at once). Every workgroup first turns the context
+// lengths into a prefix sum of blocks per sequence (in LDS); the blocks of the
+// whole batch, laid end to end, are then cut into one contiguous range per
+// wavefront, so ragged batches are balanced and every wave streams several
+// blocks. A wave walks its range one sequence segment at a time: it loads
+// that sequence's queries, weights and the page numbers of up to 64 blocks
+// (one per lane), then streams the blocks through a ring of eight 16-key
+// tiles held in registers; each tile buffer is refilled with the same tile of
+// the next block as soon as it has been consumed, so about one block (8.5 KB)
+// per wave is always in flight, and the loop body is straight-line so the
+// load counters stay exact.
 //
-// Operand layout of v_mfma_f32_32x32x16_bf16 (checked on gfx950): lane l
-// supplies A[row l%32][k = 8*(l/32) + e] and B[k = 8*(l/32) + e][col l%32],
-// e = 0..7, and receives D[row 8*(r/4) + 4*(l/32) + r%4][col l%32] in
-// register r = 0..15. The k order inside a step is free as long as A and B
-// agree: lane half c = l/32 takes the contiguous dims 32c..32c+31 of its key
-// and uses dims 32c + 8s + e in step s.
+// Matrix cores. The dot products of all T_q*H_i query rows with 16 keys are
+// v_mfma_f32_16x16x32_bf16 chains (2 steps over the 64 dims per row tile of
+// 16 query rows). Operand layout (checked on gfx950): lane l supplies
+// A[row l%16][k = 8*(l/16) + e], B[k = 8*(l/16) + e][col l%16], e = 0..7, and
+// receives D[row 4*(l/16) + r][col l%16], r = 0..3. Columns are keys, so the
+// four lanes l%16 + 16g (g = 0..3) of a key together hold its whole 64-byte
+// FP8 row: lane group g loads dims 16g..16g+15 with one 16-byte load, and one
+// load instruction covers 16 consecutive keys = 1 KB of contiguous memory. In
+// step s lane group g uses dims 16g + 8s + e (A and B agree on this order).
+// FP8 codes widen exactly to bf16 with the hardware converter.
+//
+// Rows. Query row (t, h) sits in row tile rho = (HP/4)*(t/4) + h/4 at row
+// 4*(t%4) + h%4 (HP = heads padded to 4 or 8). Lane group g thus receives
+// all heads of token 4*tau + g for every token tile tau, so the head sum, the
+// ReLU and the weights need no cross-lane traffic. The per-token key scale
+// is applied after the head sum:
+//     sum_h w_h max(0, ks*d_h) = ks * sum_h w_h med3(d_h, 0, ks >= 0 ? inf : -inf)
+// for either sign of ks. The block max over the 16 keys of a lane group is a
+// 4-step DPP reduction inside one 16-lane row.
 #include "fmt.hpp"
 #include "msa_internal.hpp"
 
@@ -32,172 +48,339 @@ namespace msa {
 
 namespace {
 
-template <bool FP8>
-struct KeyTile;
+// Key loads stream through the caches once: nontemporal unless built with
+// MSA_IDX_NT=0.
+#ifndef MSA_IDX_NT
+#define MSA_IDX_NT 1
+#endif
+constexpr int kIdxAux = MSA_IDX_NT ? kAuxNT : 0;
 
+// This lane's share of one tile (16 keys x 64 dims): key 16k + l%16,
+// dims 16*(l/16) .. 16*(l/16) + 15.
+template <bool FP8>
+struct KTile;
 template <>
-struct KeyTile<true> {  // 32 FP8 codes + the key's fp32 scale, per tile
-  u32x4 v[4][2];
-  float s[4];
+struct KTile<true> {
+  u32x4 v;   // 16 E4M3 codes
+  float s;   // the key's fp32 scale
 };
 template <>
-struct KeyTile<false> {  // 32 bf16 values per tile
-  u32x4 v[4][4];
+struct KTile<false> {
+  u32x4 v[2];  // 16 bf16 values
 };
 
+// Lane offset (bytes) of this lane's share of tile 0 inside a page; tile k
+// adds 16*k keys.
 template <bool FP8>
-__device__ __forceinline__ void load_block(const IndexerArgs& a, int page, int lane, KeyTile<FP8>& kt) {
-  const int j = lane & 31, c = lane >> 5;
+__device__ __forceinline__ uint32_t ktile_lane_off(int lane) {
+  return (uint32_t)((lane & 15) * kIdxDim + 16 * (lane >> 4)) * (FP8 ? 1u : 2u);
+}
+
+// Buffer resources of one page's keys and scales (uniform). An absent page
+// gets an empty range, so its loads return zeros without a memory access.
+template <bool FP8>
+struct PageRsrc {
+  __amdgpu_buffer_rsrc_t keys, scales;
+};
+template <bool FP8>
+__device__ __forceinline__ PageRsrc<FP8> page_rsrc(const IndexerArgs& a, int page, bool absent) {
+  constexpr uint32_t kPageBytes = kBlock * kIdxDim * (FP8 ? 1 : 2);
+  const int pg = absent ? 0 : page;
+  PageRsrc<FP8> r;
+  r.keys = make_rsrc(a.idx_k + (size_t)pg * kPageBytes, absent ? 0u : kPageBytes);
+  if constexpr (FP8) r.scales = make_rsrc(a.idx_k_scale + (size_t)pg * kBlock, absent ? 0u : kBlock * 4u);
+  return r;
+}
+
+template <bool FP8>
+__device__ __forceinline__ void load_ktile(const PageRsrc<FP8>& r, int k, int lane, uint32_t loff, KTile<FP8>& t) {
+  constexpr uint32_t kTileBytes = 16 * kIdxDim * (FP8 ? 1 : 2);
+  // the tile offset goes to the scalar offset: one offset register per lane
+  const uint32_t soff = kTileBytes * k, voff = loff;
   if constexpr (FP8) {
-    const uint8_t* base = a.idx_k + (size_t)page * (kBlock * kIdxDim);
-#pragma unroll
-    for (int tile = 0; tile < 4; tile++) {
-      const u32x4* p = reinterpret_cast<const u32x4*>(base + (tile * 32 + j) * kIdxDim + 32 * c);
-      kt.v[tile][0] = p[0];
-      kt.v[tile][1] = p[1];
-      kt.s[tile] = a.idx_k_scale[(size_t)page * kBlock + tile * 32 + j];
-    }
+    t.v = buf_load16<kIdxAux>(r.keys, voff, soff);
+    t.s = buf_load4f<kIdxAux>(r.scales, (uint32_t)(4 * (lane & 15)), (uint32_t)(64 * k));
   } else {
-    const uint16_t* base = reinterpret_cast<const uint16_t*>(a.idx_k) + (size_t)page * (kBlock * kIdxDim);
-#pragma unroll
-    for (int tile = 0; tile < 4; tile++) {
-      const u32x4* p = reinterpret_cast<const u32x4*>(base + (tile * 32 + j) * kIdxDim + 32 * c);
-#pragma unroll
-      for (int s = 0; s < 4; s++) kt.v[tile][s] = p[s];
-    }
+    t.v[0] = buf_load16<kIdxAux>(r.keys, voff, soff);
+    t.v[1] = buf_load16<kIdxAux>(r.keys, voff + 16, soff);
   }
 }
 
-// HP: padded heads per query token in the row layout (row = t*HP + h);
-// TQ: query tokens (compile-time) -- TQ*HP <= 32.
+// DPP lane moves (gfx9 encodings): quad_perm and row_ror.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, v), __builtin_bit_cast(int, v),
+                                                                 CTRL, 0xF, 0xF, false));
+}
+
+// Max over each 16-lane row; every lane of the row receives it.
+__device__ __forceinline__ float row_max(float v) {
+  v = fmaxf(v, dpp_f<0xB1>(v));    // quad_perm [1,0,3,2]
+  v = fmaxf(v, dpp_f<0x4E>(v));    // quad_perm [2,3,0,1]
+  v = fmaxf(v, dpp_f<0x124>(v));   // row_ror:4
+  v = fmaxf(v, dpp_f<0x128>(v));   // row_ror:8
+  return v;
+}
+
+// Compile-time shape: HP heads per token (4 or 8), TQ query tokens.
+template <int HP, int TQ>
+struct Shape {
+  static constexpr int HQ = HP / 4;               // row tiles per token tile
+  static constexpr int NTT = (TQ + 3) / 4;        // token tiles
+  static constexpr int RT = HQ * NTT;             // row tiles
+};
+
+// Per-sequence state of a wave: A operands, weights, positions.
 template <bool FP8, int HP, int TQ>
-__global__ __launch_bounds__(256) void indexer_pool_kernel(IndexerArgs a) {
-  static_assert(TQ * HP <= 32, "query rows exceed one 32-row MFMA tile");
-  // register groups r/4 that can hold a real token
-  constexpr int NG = (HP == 8) ? TQ : (TQ + 1) / 2;
-  const int lane = lane_id();
-  const int wave = threadIdx.x >> 6;
-  const int b = blockIdx.y;
-  const int c = lane >> 5;
-  const int j = lane & 31;
-  const int Lc = clamp_ctx(a.ctx_lens[b], a.maxb);
-  const int nblk = (Lc + kBlock - 1) / kBlock;
-  const int cover = a.scores ? a.maxb : nblk;  // scores are written for every block
-  const int blk0 = (blockIdx.x * 4 + wave) * a.ppw;
-  if (blk0 >= cover) return;
-  const int blk1 = min(blk0 + a.ppw, cover);
+struct SeqState {
+  typedef Shape<HP, TQ> S;
+  bf16x8 qa[S::RT][2];
+  float wr[S::NTT][HP];   // weight of (token 4*tau + g, head h)
+  int pt[S::NTT];         // position of token 4*tau + g
+};
 
-  // A operand: query row i = j (t = i / HP, h = i % HP), dims 32c + 8s + e.
-  bf16x8 qa[4];
-  {
-    const int t = j / HP, h = j % HP;
+template <bool FP8, int HP, int TQ>
+__device__ __forceinline__ void load_seq(const IndexerArgs& a, int b, int Lc, int lane, SeqState<FP8, HP, TQ>& st) {
+  typedef Shape<HP, TQ> S;
+  const int g = lane >> 4, rr = lane & 15;
+#pragma unroll
+  for (int rho = 0; rho < S::RT; rho++) {
+    const int t = 4 * (rho / S::HQ) + (rr >> 2), h = 4 * (rho % S::HQ) + (rr & 3);
     const bool ok = (t < a.Tq) && (h < a.Hi);
-    const uint16_t* qrow = a.idx_q + ((size_t)(b * a.Tq + t) * a.Hi + h) * kIdxDim + 32 * c;
+    // FP8 keys: step s uses dims 16g + 8s + e; bf16 keys load dims 16g.. too
+    const u32x4* q = reinterpret_cast<const u32x4*>(a.idx_q + ((size_t)(b * a.Tq + t) * a.Hi + h) * kIdxDim + 16 * g);
 #pragma unroll
-    for (int s = 0; s < 4; s++) {
-      u32x4 v = ok ? reinterpret_cast<const u32x4*>(qrow)[s] : u32x4{0, 0, 0, 0};
-      qa[s] = __builtin_bit_cast(bf16x8, v);
-    }
+    for (int s = 0; s < 2; s++) st.qa[rho][s] = __builtin_bit_cast(bf16x8, ok ? q[s] : u32x4{0, 0, 0, 0});
   }
-  // head weight of output register r: row 8*(r/4) + 4c + r%4
-  float wr[4 * NG];
-  int tg[NG];
 #pragma unroll
-  for (int g = 0; g < NG; g++) {
-    tg[g] = (HP == 8) ? g : 2 * g + c;
+  for (int tau = 0; tau < S::NTT; tau++) {
+    const int t = 4 * tau + g;
 #pragma unroll
-    for (int rr = 0; rr < 4; rr++) {
-      const int row = 8 * g + 4 * c + rr;
-      const int t = row / HP, h = row % HP;
-      wr[4 * g + rr] = (t < a.Tq && h < a.Hi) ? a.idx_w[(size_t)(b * a.Tq + t) * a.Hi + h] : 0.0f;
-    }
-  }
-  int pt[NG];
-#pragma unroll
-  for (int g = 0; g < NG; g++) pt[g] = Lc - a.Tq + tg[g];
-  // lanes that write token tg[g]: with HP == 8 the two halves hold the same total
-  const bool writer = (HP == 8) ? (c == 0) : true;
-
-  auto page_of = [&](int blk) -> int {
-    if (blk >= nblk) return -1;
-    int pg = a.block_table[(size_t)b * a.maxb + blk];
-    return (pg >= 0 && pg < a.num_pages) ? pg : -1;
-  };
-
-  KeyTile<FP8> cur, nxt;
-  int page_cur = page_of(blk0);
-  if (page_cur >= 0) load_block<FP8>(a, page_cur, lane, cur);
-
-  for (int blk = blk0; blk < blk1; blk++) {
-    const int page_nxt = (blk + 1 < blk1) ? page_of(blk + 1) : -1;
-    if (page_nxt >= 0) load_block<FP8>(a, page_nxt, lane, nxt);
-
-    float mx[NG];
-#pragma unroll
-    for (int g = 0; g < NG; g++) mx[g] = -INFINITY;
-
-#pragma unroll
-    for (int tile = 0; tile < 4; tile++) {
-      const int pos = blk * kBlock + tile * 32 + j;
-      float tot[NG];
-      if (page_cur >= 0) {
-        f32x16 acc = {};
-#pragma unroll
-        for (int s = 0; s < 4; s++) {
-          bf16x8 kb;
-          if constexpr (FP8) {
-            const u32x4 h = cur.v[tile][s >> 1];
-            kb = __builtin_bit_cast(bf16x8, (s & 1) ? fp8x8_bf16(h.z, h.w) : fp8x8_bf16(h.x, h.y));
-          } else {
-            kb = __builtin_bit_cast(bf16x8, cur.v[tile][s]);
-          }
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[s], kb, acc, 0, 0, 0);
-        }
-        float ks = 1.0f;
-        if constexpr (FP8) ks = cur.s[tile];
-#pragma unroll
-        for (int g = 0; g < NG; g++) {
-          float part = 0.0f;
-#pragma unroll
-          for (int rr = 0; rr < 4; rr++) part = fmaf(wr[4 * g + rr], fmaxf(acc[4 * g + rr] * ks, 0.0f), part);
-          if constexpr (HP == 8) part += shfl_xor(part, 32);
-          tot[g] = part;
-        }
-      } else {
-#pragma unroll
-        for (int g = 0; g < NG; g++) tot[g] = -INFINITY;
-      }
-#pragma unroll
-      for (int g = 0; g < NG; g++) {
-        const float sc = (pos <= pt[g]) ? tot[g] : -INFINITY;
-        if (a.scores && writer && tg[g] < a.Tq)
-          a.scores[((size_t)(b * a.Tq + tg[g])) * a.maxb * kBlock + pos] = sc;
-        mx[g] = fmaxf(mx[g], sc);
-      }
-    }
-    if (a.pooled) {
-#pragma unroll
-      for (int g = 0; g < NG; g++) {
-        float m = mx[g];
-#pragma unroll
-        for (int off = 1; off < 32; off <<= 1) m = fmaxf(m, shfl_xor(m, off));
-        if (j == 0 && writer && tg[g] < a.Tq) a.pooled[((size_t)(b * a.Tq + tg[g])) * a.maxb + blk] = m;
-      }
-    }
-    cur = nxt;
-    page_cur = page_nxt;
+    for (int h = 0; h < HP; h++)
+      st.wr[tau][h] = (t < a.Tq && h < a.Hi) ? a.idx_w[(size_t)(b * a.Tq + t) * a.Hi + h] : 0.0f;
+    st.pt[tau] = Lc - a.Tq + t;
   }
 }
 
-template <bool FP8, int HP>
-hipError_t launch_hp(const IndexerArgs& a, dim3 grid, hipStream_t s) {
+// Scores of one block held in the ring T (8 tiles of 16 keys); refills the
+// ring with the next block when PREFETCH. mx[tau]: this lane's max over its
+// keys for token 4*tau + g.
+template <bool FP8, int HP, int TQ, bool PREFETCH, bool SCORES>
+__device__ __forceinline__ void score_block(const IndexerArgs& a, KTile<FP8> (&T)[8], const SeqState<FP8, HP, TQ>& st,
+                                            int b, int lane, uint32_t loff, int blk, bool absent,
+                                            const PageRsrc<FP8>& rn, float (&mx)[Shape<HP, TQ>::NTT]) {
+  typedef Shape<HP, TQ> S;
+  const int g = lane >> 4;
+#pragma unroll
+  for (int tau = 0; tau < S::NTT; tau++) mx[tau] = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < 8; k++) {
+    bf16x8 kb[2];
+    if constexpr (FP8) {
+      kb[0] = __builtin_bit_cast(bf16x8, fp8x8_bf16(T[k].v.x, T[k].v.y));
+      kb[1] = __builtin_bit_cast(bf16x8, fp8x8_bf16(T[k].v.z, T[k].v.w));
+    } else {
+      kb[0] = __builtin_bit_cast(bf16x8, T[k].v[0]);
+      kb[1] = __builtin_bit_cast(bf16x8, T[k].v[1]);
+    }
+    float ks = 1.0f;
+    if constexpr (FP8) ks = T[k].s;
+    if constexpr (PREFETCH) load_ktile<FP8>(rn, k, lane, loff, T[k]);
+    f32x4 acc[S::RT];
+#pragma unroll
+    for (int rho = 0; rho < S::RT; rho++) {
+      acc[rho] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(st.qa[rho][0], kb[0], f32x4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+      acc[rho] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(st.qa[rho][1], kb[1], acc[rho], 0, 0, 0);
+    }
+    const float bound = ks >= 0.0f ? INFINITY : -INFINITY;
+    const int pos = blk * kBlock + 16 * k + (lane & 15);
+#pragma unroll
+    for (int tau = 0; tau < S::NTT; tau++) {
+      float part = 0.0f;
+#pragma unroll
+      for (int h = 0; h < HP; h++)
+        part = fmaf(st.wr[tau][h], __builtin_amdgcn_fmed3f(acc[tau * S::HQ + h / 4][h % 4], 0.0f, bound), part);
+      const float sc = (!absent && pos <= st.pt[tau]) ? part * ks : -INFINITY;
+      if constexpr (SCORES) {
+        const int t = 4 * tau + g;
+        if (t < a.Tq) a.scores[((size_t)(b * a.Tq + t)) * a.maxb * kBlock + pos] = sc;
+      }
+      mx[tau] = fmaxf(mx[tau], sc);
+    }
+    // keep the tiles in order: one tile's temporaries live at a time
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// Work blocks of sequence b: every block up to the context's last one, or
+// every column of the block table when all scores are written.
+template <bool SCORES>
+__device__ __forceinline__ int work_blocks(const IndexerArgs& a, int b) {
+  if constexpr (SCORES) return a.maxb;
+  const int Lc = clamp_ctx(a.ctx_lens[b], a.maxb);
+  return (Lc + kBlock - 1) / kBlock;
+}
+
+// Waves per SIMD each instantiation is compiled for (its register budget:
+// 4 -> 128 VGPRs, 3 -> 168, 2 -> 256). bf16 keys need twice the ring.
+constexpr int indexer_occupancy(bool fp8, int hp, int tq) {
+  return !fp8 ? 2 : (hp == 4 && tq > 4) ? 3 : 4;
+}
+
+// SCORES: write every key's score instead of the pooled block maxima.
+template <bool FP8, int HP, int TQ, bool SCORES>
+__global__ __launch_bounds__(256, indexer_occupancy(FP8, HP, TQ)) void indexer_pool_kernel(IndexerArgs a) {
+  typedef Shape<HP, TQ> S;
+  static_assert(S::RT <= 2, "at most 32 query rows");
+  extern __shared__ int32_t prefix[];  // [B + 1]: first work block of each sequence
+  __shared__ int32_t wsum[4];
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  const uint32_t loff = ktile_lane_off<FP8>(lane);
+
+  // ---- prefix sum of work blocks over the batch (each thread: a run of
+  // consecutive sequences)
+  {
+    const int per = (a.B + 255) / 256;
+    int tot = 0;
+    for (int i = 0; i < per; i++) {
+      const int bb = tid * per + i;
+      if (bb < a.B) tot += work_blocks<SCORES>(a, bb);
+    }
+    int incl = tot;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(incl, off, kWave);
+      if (lane >= off) incl += y;
+    }
+    if (lane == 63) wsum[wave] = incl;
+    __syncthreads();
+    int run = incl - tot;
+    for (int w = 0; w < wave; w++) run += wsum[w];
+    for (int i = 0; i < per; i++) {
+      const int bb = tid * per + i;
+      if (bb < a.B) {
+        prefix[bb] = run;
+        run += work_blocks<SCORES>(a, bb);
+      }
+    }
+    if (tid == 0) prefix[a.B] = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+    __syncthreads();
+  }
+  // values read from LDS land in vector registers: make the uniform ones
+  // scalar again so that loop control and addresses stay in SGPRs
+  const int64_t total = __builtin_amdgcn_readfirstlane(prefix[a.B]);
+  const int64_t NW = (int64_t)gridDim.x * 4;
+  const int64_t W = (int64_t)blockIdx.x * 4 + wave;
+  int64_t gcur = W * total / NW;
+  const int64_t gend = (W + 1) * total / NW;
+
+  while (gcur < gend) {
+    // sequence of block gcur: prefix[b] <= gcur < prefix[b + 1]
+    int lo = 0, hi = a.B;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (__builtin_amdgcn_readfirstlane(prefix[mid]) <= gcur) lo = mid;
+      else hi = mid;
+    }
+    const int b = __builtin_amdgcn_readfirstlane(lo);
+    const int seq_first = __builtin_amdgcn_readfirstlane(prefix[b]);
+    const int seq_next = __builtin_amdgcn_readfirstlane(prefix[b + 1]);
+    const int64_t seg_end = min(gend, (int64_t)seq_next);
+    const int blk_first = (int)(gcur - seq_first);
+    const int Lc = clamp_ctx(a.ctx_lens[b], a.maxb);
+    const int nblk = (Lc + kBlock - 1) / kBlock;
+    SeqState<FP8, HP, TQ> st;
+    load_seq<FP8, HP, TQ>(a, b, Lc, lane, st);
+
+    for (int w0 = blk_first; w0 < blk_first + (int)(seg_end - gcur); w0 += 64) {
+      const int nb = min(64, blk_first + (int)(seg_end - gcur) - w0);
+      // page of block w0 + lane (-1: absent or past the context)
+      int mypage = -1;
+      if (lane < nb && w0 + lane < nblk) {
+        const int pg = a.block_table[(size_t)b * a.maxb + w0 + lane];
+        if (pg >= 0 && pg < a.num_pages) mypage = pg;
+      }
+      KTile<FP8> T[8];
+      {
+        const int pg = __builtin_amdgcn_readfirstlane(mypage);
+        const PageRsrc<FP8> r0 = page_rsrc<FP8>(a, pg, pg < 0);
+#pragma unroll
+        for (int k = 0; k < 8; k++) load_ktile<FP8>(r0, k, lane, loff, T[k]);
+      }
+      // P[tau][g2]: lane i holds the max of block w0 + i for token 4*tau + g2
+      float P[S::NTT][4];
+#pragma unroll
+      for (int tau = 0; tau < S::NTT; tau++)
+#pragma unroll
+        for (int g2 = 0; g2 < 4; g2++) P[tau][g2] = -INFINITY;
+      float mx[S::NTT];
+      auto keep_max = [&](int i) {
+        if constexpr (!SCORES) {
+#pragma unroll
+          for (int tau = 0; tau < S::NTT; tau++) {
+            const float m = row_max(mx[tau]);
+#pragma unroll
+            for (int g2 = 0; g2 < 4; g2++) {
+              const float v = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, m), 16 * g2));
+              P[tau][g2] = (lane == i) ? v : P[tau][g2];
+            }
+          }
+        }
+      };
+      int i = 0;
+      for (; i + 1 < nb; i++) {
+        const bool absent = __builtin_amdgcn_readlane(mypage, i) < 0;
+        const int pgn = __builtin_amdgcn_readlane(mypage, i + 1);
+        const PageRsrc<FP8> rn = page_rsrc<FP8>(a, pgn, pgn < 0);
+        score_block<FP8, HP, TQ, true, SCORES>(a, T, st, b, lane, loff, w0 + i, absent, rn, mx);
+        keep_max(i);
+      }
+      {
+        const bool absent = __builtin_amdgcn_readlane(mypage, i) < 0;
+        score_block<FP8, HP, TQ, false, SCORES>(a, T, st, b, lane, loff, w0 + i, absent, PageRsrc<FP8>{}, mx);
+        keep_max(i);
+      }
+      if constexpr (!SCORES) {
+        if (lane < nb) {
+#pragma unroll
+          for (int tau = 0; tau < S::NTT; tau++)
+#pragma unroll
+            for (int g2 = 0; g2 < 4; g2++) {
+              const int t = 4 * tau + g2;
+              if (t < a.Tq) a.pooled[((size_t)(b * a.Tq + t)) * a.maxb + w0 + lane] = P[tau][g2];
+            }
+        }
+      }
+    }
+    gcur = seg_end;
+  }
+}
+
+// Persistent grid: the workgroups resident at once (register and LDS
+// limits), capped by the blocks the batch can have (4 waves per workgroup).
+int persistent_grid(const IndexerArgs& a, int occupancy, size_t lds) {
+  int64_t per_cu = occupancy;  // 4 waves per workgroup: one per SIMD
+  const int64_t lds_cap = (int64_t)(160 * 1024) / (int64_t)(lds + 16);
+  if (per_cu > lds_cap) per_cu = lds_cap;
+  if (per_cu > a.wgs_per_cu) per_cu = a.wgs_per_cu;
+  if (per_cu < 1) per_cu = 1;
+  int64_t grid = per_cu * a.cus;
+  const int64_t need = ((int64_t)a.B * a.maxb + 3) / 4;
+  if (grid > need) grid = need;
+  return (int)(grid < 1 ? 1 : grid);
+}
+
+template <bool FP8, int HP, bool SCORES>
+hipError_t launch_hp(const IndexerArgs& a, hipStream_t s) {
+  const size_t lds = ((size_t)a.B + 1) * sizeof(int32_t);
   switch (a.Tq) {
-#define MSA_TQ_CASE(T)                                                       \
-  case T:                                                                    \
-    if constexpr (T * HP <= 32) {                                            \
-      indexer_pool_kernel<FP8, HP, T><<<grid, 256, 0, s>>>(a);               \
-      return hipGetLastError();                                              \
-    }                                                                        \
+#define MSA_TQ_CASE(T)                                                                                 \
+  case T:                                                                                              \
+    if constexpr (Shape<HP, T>::RT <= 2) {                                                             \
+      const int grid = persistent_grid(a, indexer_occupancy(FP8, HP, T), lds);                         \
+      indexer_pool_kernel<FP8, HP, T, SCORES><<<grid, 256, lds, s>>>(a);                               \
+      return hipGetLastError();                                                                        \
+    }                                                                                                  \
     break;
     MSA_TQ_CASE(1)
     MSA_TQ_CASE(2)
@@ -217,10 +400,14 @@ hipError_t launch_hp(const IndexerArgs& a, dim3 grid, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_indexer(const IndexerArgs& a, bool fp8, int hp, hipStream_t s) {
-  const int waves_per_seq = (a.maxb + a.ppw - 1) / a.ppw;
-  dim3 grid((waves_per_seq + 3) / 4, a.B);
-  if (fp8) return hp == 8 ? launch_hp<true, 8>(a, grid, s) : launch_hp<true, 4>(a, grid, s);
-  return hp == 8 ? launch_hp<false, 8>(a, grid, s) : launch_hp<false, 4>(a, grid, s);
+  if ((a.scores != nullptr) == (a.pooled != nullptr)) return hipErrorInvalidValue;
+  if (a.B < 1 || a.B > kIndexerMaxSeqs || a.cus < 1 || a.wgs_per_cu < 1) return hipErrorInvalidValue;
+  if (a.scores) {
+    if (fp8) return hp == 8 ? launch_hp<true, 8, true>(a, s) : launch_hp<true, 4, true>(a, s);
+    return hp == 8 ? launch_hp<false, 8, true>(a, s) : launch_hp<false, 4, true>(a, s);
+  }
+  if (fp8) return hp == 8 ? launch_hp<true, 8, false>(a, s) : launch_hp<true, 4, false>(a, s);
+  return hp == 8 ? launch_hp<false, 8, false>(a, s) : launch_hp<false, 4, false>(a, s);
 }
 
 }  // namespace msa

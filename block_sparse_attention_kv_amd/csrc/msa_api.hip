@@ -53,7 +53,7 @@ msa_status_t check_params(const msa_params_t* p) {
                 p->q_len, p->idx_heads);
   if (p->max_blocks_per_seq > MSA_MAX_BLOCKS)
     return fail(MSA_ERR_UNSUPPORTED, "max_blocks_per_seq %d > %d", p->max_blocks_per_seq, MSA_MAX_BLOCKS);
-  if (p->num_seqs > 65535) return fail(MSA_ERR_UNSUPPORTED, "num_seqs %d > 65535", p->num_seqs);
+  if (p->num_seqs > MSA_MAX_SEQS) return fail(MSA_ERR_UNSUPPORTED, "num_seqs %d > %d", p->num_seqs, MSA_MAX_SEQS);
   if ((int64_t)p->num_seqs * p->q_len * p->num_kv_heads > 0x7FFFFFFF)
     return fail(MSA_ERR_UNSUPPORTED, "too many (sequence, token, head) items");
   if (p->kv_dtype != MSA_KV_BF16 && p->kv_dtype != MSA_KV_NVFP4)
@@ -102,13 +102,21 @@ Layout layout(const msa_params_t* p) {
   return L;
 }
 
-// Blocks per indexer wave: enough waves to fill 256 CUs several times over.
-int indexer_ppw(const msa_params_t* p) {
-  const int64_t blocks = (int64_t)p->num_seqs * p->max_blocks_per_seq;
-  int64_t ppw = blocks / 8192;
-  if (ppw < 1) ppw = 1;
-  if (ppw > 8) ppw = 8;
-  return (int)ppw;
+// Compute units of the current device (the persistent indexer grid is sized
+// from it).
+#ifndef MSA_INDEXER_WGS_PER_CU
+#define MSA_INDEXER_WGS_PER_CU 4
+#endif
+int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
 }
 
 // Waves per attention workgroup: about 2048 waves in flight, at most one
@@ -136,7 +144,8 @@ IndexerArgs indexer_args(const msa_params_t* p, const msa_cache_t* c, const void
   a.Hi = p->idx_heads;
   a.maxb = p->max_blocks_per_seq;
   a.num_pages = p->num_pages;
-  a.ppw = indexer_ppw(p);
+  a.cus = device_cus();
+  a.wgs_per_cu = MSA_INDEXER_WGS_PER_CU;
   return a;
 }
 

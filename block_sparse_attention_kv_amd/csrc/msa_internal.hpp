@@ -16,8 +16,13 @@ struct IndexerArgs {
   const float* idx_w;          // [B][Tq][Hi]
   float* pooled;               // [B][Tq][maxb] or nullptr
   float* scores;               // [B][Tq][maxb*128] or nullptr
-  int B, Tq, Hi, maxb, num_pages, ppw;
+  int B, Tq, Hi, maxb, num_pages;
+  int cus;                     // compute units of the device
+  int wgs_per_cu;              // cap on resident workgroups per CU (tuning)
 };
+
+// The indexer keeps a prefix sum of blocks per sequence in LDS.
+constexpr int kIndexerMaxSeqs = 8192;
 
 // Pool (optional) + top-k block selection per (sequence, query token).
 struct SelectArgs {

@@ -102,6 +102,7 @@ extern "C" {
 #define MSA_MAX_TOP_K 16     /* blocks attended per query token */
 #define MSA_MAX_BLOCKS 8192  /* max_blocks_per_seq limit (1,048,576 tokens) */
 #define MSA_MAX_GROUP 16     /* num_q_heads / num_kv_heads limit */
+#define MSA_MAX_SEQS 8192    /* num_seqs limit */
 #define MSA_NUM_STAGES 3     /* kernels enqueued by msa_decode_layer */
 
 typedef enum {
@@ -119,7 +120,8 @@ typedef enum { MSA_IDX_BF16 = 0, MSA_IDX_FP8_E4M3 = 1 } msa_idx_dtype_t;
  * block_size 128, 1 <= top_k <= 16, keep_last in {0,1},
  * num_q_heads % num_kv_heads == 0 with a group of at most 16 query heads,
  * 1 <= idx_heads, and either (q_len <= 4, idx_heads <= 8) or
- * (q_len <= 8, idx_heads <= 4); 1 <= max_blocks_per_seq <= 8192. */
+ * (q_len <= 8, idx_heads <= 4); 1 <= max_blocks_per_seq <= 8192;
+ * 1 <= num_seqs <= 8192. */
 typedef struct {
   int32_t num_seqs;           /* B */
   int32_t q_len;              /* T_q: query tokens per sequence (same for all) */

@@ -2,20 +2,26 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 3]
 
-A step is one call of msa_decode_layer (indexer + pool, select, sparse
-attention) over one batch of the chosen synthetic configuration, inputs
-resident in HBM. Consecutive steps rotate over R device replicas of the
-inputs so that no step finds its bytes in the 256 MB Infinity Cache. Prints
-one JSON line on stdout (details on stderr):
+A step is one call of msa_decode_layer (kernel 1: indexer + per-block max
+pool; kernel 2: top-16 selection + sparse attention) over one batch of the
+chosen synthetic configuration, inputs resident in HBM. Consecutive steps
+rotate over R device replicas of the inputs so that no step finds its bytes
+in the 256 MB Infinity Cache. The K timed steps lie between two HIP events on
+the launch stream. A second pass over the same K steps has every kernel's
+dispatch record its own start and end events (hipExtLaunchKernel), which
+give the per-kernel durations.
+Prints one JSON line on stdout (details on stderr):
 
   value        decode tokens/s per layer = B * T_q / step time
   roofline     the dominant kernel (the indexer scan): algorithmic bytes per
-               launch / its average duration (HIP events on the launch
-               stream), against the 8 TB/s HBM peak
+               launch / its average duration, against the 8 TB/s HBM peak;
+               traffic = HBM bytes per launch from rocprofv3 counters, when a
+               record for the current kernel source exists (else null)
   cpu_baseline the float64 oracle on a bounded sample of the same workload,
                timed on this host's cores
 """
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -27,10 +33,22 @@ import numpy as np
 HBM_PEAK_GBPS = 8000.0
 METRIC = "MSA decode tokens/s per layer at 128K ctx; achieved HBM GB/s vs 8 TB/s peak"
 ROOT = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(ROOT, "block_sparse_attention_kv_amd", "csrc")
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "traffic.json")
+# sources that define the indexer kernel's memory traffic
+INDEXER_SOURCES = ("indexer.hip", "fmt.hpp", "msa_internal.hpp")
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def source_sha(names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(CSRC, n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 # ------------------------------------------------------------ byte models
@@ -48,17 +66,66 @@ def indexer_bytes(w):
 
 
 def attention_bytes(w, sel):
-    """Algorithmic bytes of the attention launch: K+V of the union of the
-    selected blocks per (sequence, KV head) -- 144 B per token per KV head
-    for NVFP4 (codes + scales of K and V), 512 B for bf16 -- plus queries,
-    selections and bf16 outputs."""
+    """Algorithmic bytes of the selection + attention launch: K+V of the
+    union of the selected blocks per (sequence, KV head) -- 144 B per token
+    per KV head for NVFP4 (codes + scales of K and V), 512 B for bf16 -- plus
+    queries, pooled scores read, selections and bf16 outputs."""
     prm = w.params
     B, Tq, Hq, G = prm["num_seqs"], prm["q_len"], prm["num_q_heads"], prm["num_kv_heads"]
     per_tok = 144 if prm["kv_dtype"] == 1 else 512
     blocks = 0
     for b in range(B):
         blocks += len(set(int(x) for x in sel[b].ravel() if x >= 0))
-    return int(blocks * G * 128 * per_tok + B * Tq * Hq * 128 * 2 * 2 + B * Tq * prm["top_k"] * 4)
+    L = np.minimum(w.ctx_lens.astype(np.int64), prm["max_blocks_per_seq"] * 128)
+    pooled = int(((L + 127) // 128).sum()) * Tq * 4
+    return int(blocks * G * 128 * per_tok + B * Tq * Hq * 128 * 2 * 2 + B * Tq * prm["top_k"] * 4 + pooled)
+
+
+def traffic_record(config_id):
+    """HBM bytes per indexer launch from the committed counter record, if it
+    was taken on the current indexer source and this workload."""
+    try:
+        rec = json.load(open(TRAFFIC_RECORD))
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha") != source_sha(INDEXER_SOURCES) or rec.get("config_id") != config_id:
+        return None
+    return rec
+
+
+def write_traffic_record(fetch_csv, write_csv, config_id):
+    """HBM bytes per indexer launch from two rocprofv3 --pmc collections of a
+    --profile-steps run (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch). Each
+    counter is scaled by what it reads for the run's 1 GiB device copy (1 GiB
+    read, 1 GiB written), so the record is in bytes actually moved."""
+    import csv
+
+    def per_kernel(path, counter):
+        vals, copy = [], None
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            v = float(r["Counter_Value"]) * 1024.0
+            if "indexer_pool_kernel" in r["Kernel_Name"]:
+                vals.append(v)
+            elif "copyBuffer" in r["Kernel_Name"] and (copy is None or v > copy):
+                copy = v          # the largest copy: the 1 GiB calibration copy
+        return vals, copy
+
+    f, fc = per_kernel(fetch_csv, "FETCH_SIZE")
+    w, wc = per_kernel(write_csv, "WRITE_SIZE")
+    gib = float(1 << 30)
+    f_scale, w_scale = gib / fc, gib / wc
+    fetch = float(np.mean(f)) * f_scale
+    write = float(np.mean(w)) * w_scale
+    rec = {"kernel": "indexer_pool", "config_id": config_id, "source_sha": source_sha(INDEXER_SOURCES),
+           "fetch_bytes_per_launch": fetch, "write_bytes_per_launch": write,
+           "traffic_bytes_per_launch": fetch + write, "fetch_scale": f_scale, "write_scale": w_scale,
+           "launches": [len(f), len(w)]}
+    os.makedirs(os.path.dirname(TRAFFIC_RECORD), exist_ok=True)
+    with open(TRAFFIC_RECORD, "w") as fh:
+        json.dump(rec, fh, indent=1)
+    print(json.dumps(rec))
 
 
 # ------------------------------------------------------------ cpu baseline
@@ -74,10 +141,9 @@ def cpu_baseline(w, gpu_res, budget_s=20.0):
     except Exception:
         threads = 1
     prm = w.params
-    order = list(range(prm["num_seqs"]))
     t0 = time.perf_counter()
-    done_tok, seqs, ties, max_err, max_ulp = 0, [], 0, 0.0, 0.0
-    for b in order:
+    done_tok, seqs, other_sel, max_err = 0, [], 0, 0.0
+    for b in range(prm["num_seqs"]):
         res = O.decode_sequence(w, b)
         done_tok += len(res)
         seqs.append(b)
@@ -86,22 +152,19 @@ def cpu_baseline(w, gpu_res, budget_s=20.0):
                 continue
             g = sorted(int(x) for x in gpu_res["sel"][b, t] if x >= 0)
             if g != list(r["sel"]):
-                ties += 1
+                other_sel += 1
             else:
                 err = np.abs(gpu_res["out"][b, t] - r["out"])
                 small = np.abs(r["out"]) < 0.5
                 if small.any():
                     max_err = max(max_err, float(err[small].max()))
-                ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(r["out"]), 2.0 ** -126))) - 7)
-                max_ulp = max(max_ulp, float(np.max(err / ulp)))
         if time.perf_counter() - t0 > budget_s:
             break
     dt = time.perf_counter() - t0
     return {"value": done_tok / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": "%d of %d sequences (%d query tokens), float64 numpy, %.1f s" % (
                 len(seqs), prm["num_seqs"], done_tok, dt),
-            "sample_check": {"tokens_with_other_selection": ties, "max_abs_where_o_below_0.5": max_err,
-                             "max_err_in_bf16_ulps": max_ulp}}
+            "sample_check": {"tokens_with_other_selection": other_sel, "max_abs_where_o_below_0.5": max_err}}
 
 
 # ------------------------------------------------------------------ main
@@ -116,12 +179,17 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-steps", type=int, default=0,
-                    help="only run this many steps (for rocprofv3 runs); no JSON checks")
+                    help="only run this many steps and a 1 GiB calibration copy (for rocprofv3 runs)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/traffic.json from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE counter "
+                         "collections of a --profile-steps run, and exit")
     args = ap.parse_args()
+    if args.traffic_from:
+        write_traffic_record(args.traffic_from[0], args.traffic_from[1], args.config)
+        return
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (the decode step of one "
-              "GPU's share is the unit; see DESIGN.md for how it would shard). Run with --gpus 1.",
-              file=sys.stderr)
+        print("bench.py measures one GPU: this build has no multi-GPU path (one GPU's share of the decode "
+              "batch is the unit of work). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -137,10 +205,7 @@ def main():
     step_guess = indexer_bytes(w) + B * prm["num_kv_heads"] * 64 * 128 * 144
     R = args.replicas or max(2, min(4, int(math.ceil(3 * 256e6 / max(step_guess, 1)))))
     dev = "cuda"
-    reps = []
-    for r in range(R):
-        params, cache, qs = msa.to_device(w, dev)
-        reps.append((params, cache, qs))
+    reps = [msa.to_device(w, dev) for _ in range(R)]
     torch.cuda.synchronize()
     log("uploaded %d replica(s) in %.1f s" % (R, time.perf_counter() - t0))
     out = torch.empty((B, Tq, Hq, 128), dtype=torch.int16, device=dev)
@@ -148,17 +213,37 @@ def main():
     sel = torch.empty((B, Tq, prm["top_k"]), dtype=torch.int32, device=dev)
     ws = msa.alloc_workspace(reps[0][0], dev)
 
+    # Every C argument is built once, so that a timed step is one C-ABI call:
+    # the host then stays ahead of the GPU and the queue never drains.
+    import ctypes
+    L = msa.load()
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    ws_bytes = ws.numel() * ws.element_size()
+    keep = []
+
+    def vp(t):
+        return ctypes.c_void_p(t.data_ptr())
+
+    call_args = []
+    for params, cache, qs in reps:
+        c = cache.c()
+        keep.append(c)
+        call_args.append([ctypes.byref(params), ctypes.byref(c), vp(qs["q"]), vp(qs["idx_q"]), vp(qs["idx_w"]),
+                          vp(out), vp(lse), vp(sel), vp(ws), ctypes.c_size_t(ws_bytes), stream])
+
     def step(i, events=None):
-        params, cache, qs = reps[i % R]
-        msa.msa_decode_layer(params, cache, qs["q"], qs["idx_q"], qs["idx_w"], out, ws, lse=lse, sel_out=sel,
-                             stage_events=events)
+        if events is None:
+            st = L.msa_decode_layer(*call_args[i % R])
+        else:
+            st = L.msa_decode_layer_traced(*call_args[i % R], events)
+        if st != 0:
+            raise RuntimeError("msa_decode_layer: %s" % L.msa_last_error().decode())
 
     if args.profile_steps:
         for i in range(args.profile_steps):
             step(i)
         torch.cuda.synchronize()
         log("profile run: %d steps done" % args.profile_steps)
-        # plain copy of a known size, for counter calibration
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
         dst.copy_(src)
@@ -173,9 +258,9 @@ def main():
                "out": (out.view(torch.int16).cpu().numpy().astype(np.uint16).astype(np.uint32) << 16)
                .view(np.float32).astype(np.float64)}
 
-    # ---- headline: K steps, no tracing
-    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # ---- timed region: K steps between two HIP events on the launch stream
     torch.cuda.synchronize()
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     wall0 = time.perf_counter()
     t_start.record()
     for i in range(args.steps):
@@ -184,20 +269,33 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_step = t_start.elapsed_time(t_end) / args.steps
-    log("timed %d steps: %.3f ms/step (events), %.3f ms/step (wall)" % (args.steps, ms_step, wall * 1e3 / args.steps))
+    log("timed %d steps: %.4f ms/step (events), %.4f ms/step (wall)" % (args.steps, ms_step,
+                                                                       wall * 1e3 / args.steps))
 
-    # ---- per-kernel durations: the same steps with stage events
+    # ---- per-kernel durations: the same K steps again, each kernel's dispatch
+    # recording its own start and end event (hipExtLaunchKernel); the events
+    # lengthen the step a little, so the step time above comes from the
+    # uninstrumented pass
     n_st = msa.NUM_STAGES
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_st + 1)] for _ in range(args.steps)]
-    for i in range(args.steps):
-        step(i, evs[i])
+    kev = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * n_st)] for _ in range(args.steps)]
+    for row in kev:          # create the HIP events before the timed pass
+        for e in row:
+            e.record()
     torch.cuda.synchronize()
-    stage_ms = [float(np.mean([evs[i][s].elapsed_time(evs[i][s + 1]) for i in range(args.steps)]))
+    ev_arrays = [(ctypes.c_void_p * (2 * n_st))(*[e.cuda_event for e in row]) for row in kev]
+    k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    k0.record()
+    for i in range(args.steps):
+        step(i, ev_arrays[i])
+    k1.record()
+    torch.cuda.synchronize()
+    ms_step_traced = k0.elapsed_time(k1) / args.steps
+    stage_ms = [float(np.mean([kev[i][2 * s].elapsed_time(kev[i][2 * s + 1]) for i in range(args.steps)]))
                 for s in range(n_st)]
-    traced_ms = float(np.mean([evs[i][0].elapsed_time(evs[i][n_st]) for i in range(args.steps)]))
-    log("stages (ms): " + ", ".join("%s %.4f" % (n, v) for n, v in zip(msa.STAGE_NAMES, stage_ms)))
+    log("kernels (ms): " + ", ".join("%s %.4f" % (n, v) for n, v in zip(msa.STAGE_NAMES, stage_ms)) +
+        "; step with kernel events %.4f ms" % ms_step_traced)
 
-    # ---- attainable copy bandwidth on this machine
+    # ---- attainable copy bandwidth on this machine (context)
     src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     dst = torch.empty_like(src)
     for _ in range(3):
@@ -215,8 +313,9 @@ def main():
     att_b = attention_bytes(w, gpu_res["sel"])
     step_b = idx_b + att_b
     idx_gbps = idx_b / (stage_ms[0] * 1e-3) / 1e9
-    att_gbps = att_b / (stage_ms[2] * 1e-3) / 1e9
+    att_gbps = att_b / (stage_ms[1] * 1e-3) / 1e9
     step_gbps = step_b / (ms_step * 1e-3) / 1e9
+    rec = traffic_record(args.config)
     tokens = B * Tq
     res = {
         "metric": METRIC,
@@ -236,11 +335,13 @@ def main():
                    "idx_heads": prm["idx_heads"], "top_k": prm["top_k"], "block": 128,
                    "input_replicas": R},
         "roofline": {"bound": "hbm", "kernel": "indexer_pool", "achieved": idx_gbps, "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": idx_gbps / HBM_PEAK_GBPS, "traffic": None,
+                     "unit": "GB/s", "frac": idx_gbps / HBM_PEAK_GBPS,
+                     "traffic": None if rec is None else rec["traffic_bytes_per_launch"],
                      "algorithmic_bytes": idx_b, "avg_ms": stage_ms[0]},
         "step": {"algorithmic_bytes": step_b, "gbps": step_gbps, "frac": step_gbps / HBM_PEAK_GBPS,
-                 "stage_ms": dict(zip(msa.STAGE_NAMES, stage_ms)), "traced_ms_per_step": traced_ms,
-                 "attention_bytes": att_b, "attention_gbps": att_gbps, "copy_gbps_attainable": copy_gbps},
+                 "stage_ms": dict(zip(msa.STAGE_NAMES, stage_ms)), "ms_per_step_with_kernel_events": ms_step_traced,
+                 "attention_bytes": att_b,
+                 "attention_gbps": att_gbps, "copy_gbps_attainable": copy_gbps},
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, gpu_res, args.cpu_budget)

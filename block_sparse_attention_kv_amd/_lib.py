@@ -18,8 +18,8 @@ LIB_PATH = os.path.join(_HERE, "libmsa.so")
 MSA_OK, MSA_ERR_INVALID_ARG, MSA_ERR_UNSUPPORTED, MSA_ERR_WORKSPACE, MSA_ERR_HIP = range(5)
 KV_BF16, KV_NVFP4 = 0, 1
 IDX_BF16, IDX_FP8 = 0, 1
-NUM_STAGES = 3
-STAGE_NAMES = ("indexer_pool", "select", "sparse_attn")
+NUM_STAGES = 2
+STAGE_NAMES = ("indexer_pool", "select_sparse_attn")
 
 
 class MSAError(RuntimeError):
@@ -190,8 +190,9 @@ def msa_sparse_attn_decode(params, cache, q, sel, out, lse=None, workspace=None,
 
 def msa_decode_layer(params, cache, q, idx_q, idx_w, out, workspace, lse=None, sel_out=None, stream=None,
                      stage_events=None):
-    """Whole decode step. stage_events: optional list of NUM_STAGES + 1
-    torch.cuda.Event(enable_timing=True), recorded around each kernel."""
+    """Whole decode step. stage_events: optional list of 2 * NUM_STAGES
+    torch.cuda.Event(enable_timing=True): the start and end of kernel i are
+    recorded into events 2i and 2i+1 by the kernel's dispatch."""
     c = cache.c()
     ws_bytes = workspace.numel() * workspace.element_size()
     L = load()
@@ -199,8 +200,8 @@ def msa_decode_layer(params, cache, q, idx_q, idx_w, out, workspace, lse=None, s
         st = L.msa_decode_layer(ctypes.byref(params), ctypes.byref(c), _ptr(q), _ptr(idx_q), _ptr(idx_w),
                                 _ptr(out), _ptr(lse), _ptr(sel_out), _ptr(workspace), ws_bytes, _stream(stream))
     else:
-        if len(stage_events) != NUM_STAGES + 1:
-            raise ValueError("need %d events" % (NUM_STAGES + 1))
+        if len(stage_events) != 2 * NUM_STAGES:
+            raise ValueError("need %d events" % (2 * NUM_STAGES))
         s = torch.cuda.current_stream() if stream is None else stream
         for e in stage_events:
             if e.cuda_event == 0:   # torch creates the HIP event lazily on first record

@@ -4,15 +4,28 @@
 // [ainewsbites page "vLLM Adds Day-0 Support for MiniMax-M3.1-Flash on NVIDIA
 // and AMD GPUs", section "A model built for efficient inference": main
 // attention runs exactly over the top 16 blocks only, at most 2,048 keys per
-// query; the KV cache is NVFP4. upstreambeat page "vLLM turns MiniMax's
-// day-zero promise into GPU-specific serving code", section "What changed":
-// NVFP4 is dequantised inside the sparse-attention kernels.]
+// query, the most recent block always among them; the KV cache is NVFP4.
+// upstreambeat page "vLLM turns MiniMax's day-zero promise into
+// GPU-specific serving code", section "What changed": NVFP4 is dequantised
+// inside the sparse-attention kernels.]
 //
 // Work split. One workgroup per (sequence, query token, KV head) with W
-// wavefronts; wave w takes the selected blocks w, w+W, ... and keeps an online
-// softmax state (running max m, sum l, output O) for the G <= 16 query heads
-// that share the KV head. The W states are merged in LDS by a fixed-order
-// tree (log-sum-exp combine), so the result is bitwise reproducible.
+// wavefronts. In the fused decode layer the workgroup first picks its query
+// token's blocks from the pooled scores (topk.hpp); the selection is cheap
+// next to the K/V traffic, so the KV heads of one token each repeat it rather
+// than wait for one another. Wave w then takes the selected blocks w, w+W, ...
+// and keeps an online softmax state (running max m, sum l, output O) for the
+// G <= 16 query heads of the KV head. The W states are merged in LDS by a
+// fixed-order tree (log-sum-exp combine), so the result is bitwise
+// reproducible.
+//
+// Streaming (NVFP4). A wave keeps the next block's loads in flight while it
+// computes the current one: the K of its next block is requested as soon as
+// S of the current block is formed, and the V as soon as the P.V product is
+// done, into the same registers. Loads go through per-block buffer resources;
+// when there is no next block the resources are empty (the loads return
+// zeros without touching memory), so the loop is straight-line code and the
+// compiler's load counters stay exact.
 //
 // Per block (128 keys) and wave:
 //   S^T = K Q^T    16x16x32 MFMA, A = K rows (keys), B = Q^T (heads): 8 key
@@ -39,6 +52,7 @@
 // scale, the V scale multiplies the output.
 #include "fmt.hpp"
 #include "msa_internal.hpp"
+#include "topk.hpp"
 
 namespace msa {
 
@@ -49,6 +63,8 @@ constexpr int kSlotFloats = 16 * kHeadDim + 32;  // O[16][128], m[16], l[16]
 __device__ __forceinline__ int kappa(int tau, int rho) {
   return 32 * (rho >> 2) + 8 * (tau >> 1) + 4 * (tau & 1) + (rho & 3);
 }
+// kappa(tau, rho) = krow(rho) + ktau(tau)
+__host__ __device__ constexpr int ktau(int tau) { return 8 * (tau >> 1) + 4 * (tau & 1); }
 
 template <bool NVFP4>
 struct MfmaT;
@@ -79,19 +95,67 @@ __device__ __forceinline__ float lse_weight(float m, float M) {
   return (m == -INFINITY) ? 0.0f : fast_exp2(m - M);
 }
 
+// ---------------------------------------------------------------- NVFP4 I/O
+
+// Buffer resources of one block of one KV head (K codes, K scales, V codes,
+// V scales); empty ranges when `none`.
+struct KvRsrc {
+  __amdgpu_buffer_rsrc_t kd, ks, vd, vs;
+};
+__device__ __forceinline__ KvRsrc nvfp4_rsrc(const AttnArgs& a, int page, int g, bool none) {
+  const size_t pg = (size_t)(none ? 0 : page) * a.Hkv + g;
+  const uint32_t n8k = none ? 0u : 8192u, n1k = none ? 0u : 1024u;
+  KvRsrc r;
+  r.kd = make_rsrc(a.k_data + pg * 8192, n8k);
+  r.ks = make_rsrc(a.k_scale + pg * 1024, n1k);
+  r.vd = make_rsrc(a.v_data + pg * 8192, n8k);
+  r.vs = make_rsrc(a.v_scale + pg * 1024, n1k);
+  return r;
+}
+
+// This lane's share of a block: K codes of key kappa(tau, l%16), dims
+// 32*(l/16) .. +31 (16 bytes), and the two E4M3 scales of those dims; V codes
+// of dim 16*dt + l%16, tokens 32*(l/16) .. +31, and 16 bytes of the [8][128]
+// V scale array.
+struct KRegs {
+  u32x4 kd[8];
+  uint32_t ks[8];
+};
+struct VRegs {
+  u32x4 vd[8];
+  u32x4 vs;
+};
+struct LaneOff {
+  uint32_t k, ks, v, vs;
+};
+
+__device__ __forceinline__ void load_k(const KvRsrc& r, const LaneOff& o, KRegs& K) {
+#pragma unroll
+  for (int tau = 0; tau < 8; tau++) {
+    K.kd[tau] = buf_load16<kAuxNT>(r.kd, o.k, (uint32_t)(64 * ktau(tau)));
+    K.ks[tau] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r.ks, (int)o.ks, 8 * ktau(tau), kAuxNT);
+  }
+}
+__device__ __forceinline__ void load_v(const KvRsrc& r, const LaneOff& o, VRegs& V) {
+#pragma unroll
+  for (int dt = 0; dt < 8; dt++) V.vd[dt] = buf_load16<kAuxNT>(r.vd, o.v, (uint32_t)(1024 * dt));
+  V.vs = buf_load16<kAuxNT>(r.vs, o.vs, 0);
+}
+
+// ---------------------------------------------------------------- kernel
+
 template <bool NVFP4, int W>
-__global__ __launch_bounds__(64 * W) void sparse_attn_kernel(AttnArgs a) {
+__global__ __launch_bounds__(64 * W, (W <= 4 ? 2 : 1)) void sparse_attn_kernel(AttnArgs a) {
   typedef MfmaT<NVFP4> MT;
   typedef typename MT::vec vec;
-  // per-wave fp16 V-scale staging during the scan; merge slots afterwards
-  constexpr int kStageBytes = W * 1024 * 2;
-  constexpr int kMergeBytes = (W / 2) * kSlotFloats * 4;
-  constexpr int kLdsBytes = kStageBytes > kMergeBytes ? kStageBytes : kMergeBytes;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
-  __shared__ int32_t blist[16], plist[16];
+  constexpr int NT = 64 * W;
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];  // select / V-scale stages / merge
+  __shared__ TopkLds tk;
+  __shared__ int32_t sel_lds[kTopkMax], blist[kTopkMax], plist[kTopkMax];
   __shared__ int32_t nlist;
 
-  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  const int tid = threadIdx.x, lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps block loops scalar
   const int item = blockIdx.x;
   const int g = item % a.Hkv;
   const int bt = item / a.Hkv;
@@ -101,14 +165,42 @@ __global__ __launch_bounds__(64 * W) void sparse_attn_kernel(AttnArgs a) {
   const int h = lane & 15;      // head within the group (MFMA column)
   const int q4 = lane >> 4;     // lane group 0..3
 
-  // ---- selected blocks that exist: compacted, order kept
+  // ---- Q^T operand: head h, dims 32*q4 + 8s + e (issued before the
+  // selection; it does not depend on it)
+  u32x4 qraw[4];
+  {
+    const bool ok = h < a.grp;
+    const uint16_t* qrow = a.q + ((size_t)bt * a.Hq + g * a.grp + h) * kHeadDim + 32 * q4;
+#pragma unroll
+    for (int s = 0; s < 4; s++) qraw[s] = ok ? reinterpret_cast<const u32x4*>(qrow)[s] : u32x4{0, 0, 0, 0};
+  }
+
+  // ---- selected blocks (fused: from the pooled scores; the block-table
+  // entries of all visible blocks are fetched in the same pass into an LDS
+  // page table, so the winners' pages need no second dependent load)
+  int nsel;
+  int32_t* pages = reinterpret_cast<int32_t*>(lds);  // [nvis], fused path only
+  const int32_t* bt_row = a.block_table + (size_t)b * a.maxb;
+  if (a.pooled) {
+    const int nvis = p < 0 ? 0 : p / kBlock + 1;
+    const float* src = a.pooled + (size_t)bt * a.maxb;
+    nsel = block_topk<NT>([&](int i) { return src[i]; }, [&](int i) { return bt_row[i]; }, pages, nvis,
+                          a.top_k, a.keep_last != 0, sel_lds, tk);
+    if (g == 0 && a.sel)
+      for (int k = tid; k < a.top_k; k += NT) a.sel[(size_t)bt * a.top_k + k] = k < nsel ? sel_lds[k] : -1;
+  } else {
+    if (tid < a.top_k) sel_lds[tid] = a.sel[(size_t)bt * a.top_k + tid];
+    nsel = a.top_k;
+    __syncthreads();
+  }
+  // blocks that exist, compacted, order kept
   if (wave == 0) {
     bool ok = false;
     int blk = -1, page = -1;
-    if (lane < a.top_k && p >= 0) {
-      blk = a.sel[(size_t)bt * a.top_k + lane];
+    if (lane < nsel && p >= 0) {
+      blk = sel_lds[lane];
       if (blk >= 0 && blk < a.maxb && blk * kBlock <= p) {
-        page = a.block_table[(size_t)b * a.maxb + blk];
+        page = a.pooled ? pages[blk] : bt_row[blk];
         ok = page >= 0 && page < a.num_pages;
       }
     }
@@ -121,49 +213,44 @@ __global__ __launch_bounds__(64 * W) void sparse_attn_kernel(AttnArgs a) {
     if (lane == 0) nlist = __popcll(bal);
   }
 
-  // ---- Q^T operand: head h, dims 32*q4 + 8s + e
   vec qb[4];
   float cscale;
-  {
-    const bool ok = h < a.grp;
-    const uint16_t* qrow = a.q + ((size_t)bt * a.Hq + g * a.grp + h) * kHeadDim + 32 * q4;
-    u32x4 raw[4];
+  if constexpr (NVFP4) {
+    float amax = 0.0f;
 #pragma unroll
-    for (int s = 0; s < 4; s++) raw[s] = ok ? reinterpret_cast<const u32x4*>(qrow)[s] : u32x4{0, 0, 0, 0};
-    if constexpr (NVFP4) {
-      float amax = 0.0f;
+    for (int s = 0; s < 4; s++)
 #pragma unroll
-      for (int s = 0; s < 4; s++)
-#pragma unroll
-        for (int e = 0; e < 4; e++) {
-          const uint32_t w = raw[s][e];
-          amax = fmaxf(amax, fmaxf(fabsf(bf16_bits_to_f32(w & 0xFFFFu)), fabsf(bf16_bits_to_f32(w >> 16))));
-        }
-      amax = fmaxf(amax, shfl_xor(amax, 16));
-      amax = fmaxf(amax, shfl_xor(amax, 32));
-      // power-of-two pre-scale keeping the row inside fp16's range
-      int sh = 0;
-      if (amax >= 32768.0f) sh = ((int)((__float_as_uint(amax) >> 23) & 255) - 127) - 14;
-      const float down = __uint_as_float((uint32_t)(127 - sh) << 23);
-      cscale = a.score_scale * __uint_as_float((uint32_t)(127 + sh) << 23);
-#pragma unroll
-      for (int s = 0; s < 4; s++) {
-        u32x4 v;
-#pragma unroll
-        for (int e = 0; e < 4; e++) {
-          const uint32_t w = raw[s][e];
-          v[e] = f32x2_to_f16x2(bf16_bits_to_f32(w & 0xFFFFu) * down, bf16_bits_to_f32(w >> 16) * down);
-        }
-        qb[s] = __builtin_bit_cast(vec, v);
+      for (int e = 0; e < 4; e++) {
+        const uint32_t w = qraw[s][e];
+        amax = fmaxf(amax, fmaxf(fabsf(bf16_bits_to_f32(w & 0xFFFFu)), fabsf(bf16_bits_to_f32(w >> 16))));
       }
-    } else {
-      cscale = a.score_scale;
+    amax = fmaxf(amax, shfl_xor(amax, 16));
+    amax = fmaxf(amax, shfl_xor(amax, 32));
+    // power-of-two pre-scale keeping the row inside fp16's range
+    int sh = 0;
+    if (amax >= 32768.0f) sh = ((int)((__float_as_uint(amax) >> 23) & 255) - 127) - 14;
+    // the sign of the score scale (a negative K tensor scale) moves into Q,
+    // so that the softmax can take the max of the raw dot products
+    const float sgn = a.score_scale < 0.0f ? -1.0f : 1.0f;
+    const float down = sgn * __uint_as_float((uint32_t)(127 - sh) << 23);
+    cscale = fabsf(a.score_scale) * __uint_as_float((uint32_t)(127 + sh) << 23);
 #pragma unroll
-      for (int s = 0; s < 4; s++) qb[s] = __builtin_bit_cast(vec, raw[s]);
+    for (int s = 0; s < 4; s++) {
+      u32x4 v;
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        const uint32_t w = qraw[s][e];
+        v[e] = f32x2_to_f16x2(bf16_bits_to_f32(w & 0xFFFFu) * down, bf16_bits_to_f32(w >> 16) * down);
+      }
+      qb[s] = __builtin_bit_cast(vec, v);
     }
+  } else {
+    cscale = a.score_scale;
+#pragma unroll
+    for (int s = 0; s < 4; s++) qb[s] = __builtin_bit_cast(vec, qraw[s]);
   }
   __syncthreads();
-  const int n = nlist;
+  const int n = __builtin_amdgcn_readfirstlane(nlist);
 
   SoftmaxState st;
   st.m = -INFINITY;
@@ -171,96 +258,41 @@ __global__ __launch_bounds__(64 * W) void sparse_attn_kernel(AttnArgs a) {
 #pragma unroll
   for (int d = 0; d < 8; d++) st.o[d] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-  // fp16 V scales of the current block: [8 groups][128 keys]
-  f16* vs_stage = reinterpret_cast<f16*>(lds) + wave * 1024;
-
-  for (int i = wave; i < n; i += W) {
-    const int blk = blist[i];
-    const size_t pg = (size_t)plist[i] * a.Hkv + g;
-    const int rho = lane & 15;
-
-    // ---- issue the block's loads
-    u32x4 kd[8];
-    uint32_t ksc[8];
-    u32x4 vd[8];
-    u32x4 vsraw;
-    if constexpr (NVFP4) {
-      const uint8_t* kb = a.k_data + pg * (kBlock * 64);
-      const uint8_t* ks = a.k_scale + pg * (kBlock * 8);
+  // raw scores of one block (S^T tiles) -> online softmax update and the P^T
+  // operand; `partial`: the block holds keys past p. cscale >= 0, so the max
+  // of the scaled scores is cscale times the max of the raw ones.
+  auto softmax_block = [&](f32x4 (&sacc)[8], int blk, bool partial, vec (&pb)[4]) {
+    float rmax = -INFINITY;
+    if (partial) {
 #pragma unroll
-      for (int tau = 0; tau < 8; tau++) {
-        const int key = kappa(tau, rho);
-        kd[tau] = *reinterpret_cast<const u32x4*>(kb + key * 64 + 16 * q4);
-        ksc[tau] = *reinterpret_cast<const uint16_t*>(ks + key * 8 + 2 * q4);
-      }
-      const uint8_t* vb = a.v_data + pg * (kHeadDim * 64);
+      for (int tau = 0; tau < 8; tau++)
 #pragma unroll
-      for (int dt = 0; dt < 8; dt++) vd[dt] = *reinterpret_cast<const u32x4*>(vb + (16 * dt + rho) * 64 + 16 * q4);
-      vsraw = *reinterpret_cast<const u32x4*>(a.v_scale + pg * 1024 + 16 * lane);
-    }
-
-    // ---- S^T = K Q^T for the 8 key tiles
-    f32x4 sacc[8];
-    if constexpr (NVFP4) {
-#pragma unroll
-      for (int tau = 0; tau < 8; tau++) {
-        const uint32_t sc2 = fp8x2_f16x2<false>(ksc[tau]);  // groups 2*q4, 2*q4+1
-        const uint32_t slo = bcast_lo16(sc2), shi = bcast_hi16(sc2);
-        f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int s = 0; s < 4; s++) {
-          const u32x4 kv = nvfp4x8_f16(kd[tau][s], s < 2 ? slo : shi);
-          acc = MT::mma(__builtin_bit_cast(vec, kv), qb[s], acc);
+        for (int r = 0; r < 4; r++) {
+          const bool vis = blk * kBlock + kappa(tau, 4 * q4 + r) <= p;
+          sacc[tau][r] = vis ? sacc[tau][r] : -INFINITY;
+          rmax = fmaxf(rmax, sacc[tau][r]);
         }
-        sacc[tau] = acc;
-      }
     } else {
-      const uint16_t* kb = reinterpret_cast<const uint16_t*>(a.k_data) + pg * (kBlock * kHeadDim);
 #pragma unroll
-      for (int tau = 0; tau < 8; tau++) {
-        const u32x4* kr = reinterpret_cast<const u32x4*>(kb + kappa(tau, rho) * kHeadDim + 32 * q4);
-        f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+      for (int tau = 0; tau < 8; tau++)
 #pragma unroll
-        for (int s = 0; s < 4; s++) acc = MT::mma(__builtin_bit_cast(vec, kr[s]), qb[s], acc);
-        sacc[tau] = acc;
-      }
+        for (int r = 0; r < 4; r++) rmax = fmaxf(rmax, sacc[tau][r]);
     }
-
-    // ---- V scales to fp16 in LDS (wave-private)
-    if constexpr (NVFP4) {
-      u32x4 lo, hi;
-      lo = fp8x8_f16(vsraw.x, vsraw.y);
-      hi = fp8x8_f16(vsraw.z, vsraw.w);
-      u32x4* dst = reinterpret_cast<u32x4*>(vs_stage + 16 * lane);
-      dst[0] = lo;
-      dst[1] = hi;
-      wave_lds_sync();
-    }
-
-    // ---- online softmax over the block (log2 domain)
-    float bmax = -INFINITY;
-#pragma unroll
-    for (int tau = 0; tau < 8; tau++)
-#pragma unroll
-      for (int r = 0; r < 4; r++) {
-        const int pos = blk * kBlock + kappa(tau, 4 * q4 + r);
-        const float v = (pos <= p) ? sacc[tau][r] * cscale : -INFINITY;
-        sacc[tau][r] = v;
-        bmax = fmaxf(bmax, v);
-      }
-    bmax = fmaxf(bmax, shfl_xor(bmax, 16));
-    bmax = fmaxf(bmax, shfl_xor(bmax, 32));
+    rmax = fmaxf(rmax, shfl_xor(rmax, 16));
+    rmax = fmaxf(rmax, shfl_xor(rmax, 32));
+    const float bmax = rmax == -INFINITY ? -INFINITY : rmax * cscale;
     const float mnew = fmaxf(st.m, bmax);
-    const float alpha = lse_weight(st.m, mnew);
     float psum = 0.0f;
-    vec pb[4];
 #pragma unroll
     for (int s = 0; s < 4; s++) {
       float pv[8];
 #pragma unroll
       for (int e = 0; e < 8; e++) {
-        pv[e] = fast_exp2(sacc[2 * s + (e >> 2)][e & 3] - mnew);
-        psum += pv[e];
+        const float x = sacc[2 * s + (e >> 2)][e & 3];
+        float v = fast_exp2(fmaf(x, cscale, -mnew));
+        if (partial) v = x == -INFINITY ? 0.0f : v;
+        pv[e] = v;
+        psum += v;
       }
       u32x4 pk;
       pk.x = MT::pack(pv[0], pv[1]);
@@ -269,24 +301,100 @@ __global__ __launch_bounds__(64 * W) void sparse_attn_kernel(AttnArgs a) {
       pk.w = MT::pack(pv[6], pv[7]);
       pb[s] = __builtin_bit_cast(vec, pk);
     }
-    st.l = st.l * alpha + psum;
-    st.m = mnew;
+    // rescale the running state only if some head's max grew
+    if (__ballot(mnew != st.m) != 0) {
+      const float alpha = lse_weight(st.m, mnew);
+      st.l *= alpha;
 #pragma unroll
-    for (int d = 0; d < 8; d++) st.o[d] *= alpha;
+      for (int d = 0; d < 8; d++) st.o[d] *= alpha;
+    }
+    st.l += psum;
+    st.m = mnew;
+  };
 
-    // ---- O^T += V^T P^T
-    if constexpr (NVFP4) {
+  if constexpr (NVFP4) {
+    // fp16 V scales of the current block: [8 groups][128 keys] per wave
+    f16* vs_stage = reinterpret_cast<f16*>(lds) + wave * 1024;
+    const int rho = lane & 15;
+    LaneOff off;
+    off.k = (uint32_t)((32 * (rho >> 2) + (rho & 3)) * 64 + 16 * q4);
+    off.ks = (uint32_t)((32 * (rho >> 2) + (rho & 3)) * 8 + 2 * q4);
+    off.v = (uint32_t)(rho * 64 + 16 * q4);
+    off.vs = (uint32_t)(16 * lane);
+    KRegs K;
+    VRegs V;
+    {
+      const bool none = wave >= n;
+      const int pg = none ? 0 : __builtin_amdgcn_readfirstlane(plist[wave]);
+      const KvRsrc r0 = nvfp4_rsrc(a, pg, g, none);
+      load_k(r0, off, K);
+      load_v(r0, off, V);
+    }
+    for (int i = wave; i < n; i += W) {
+      const int blk = __builtin_amdgcn_readfirstlane(blist[i]);
+      const bool none = i + W >= n;
+      const int pgn = none ? 0 : __builtin_amdgcn_readfirstlane(plist[i + W]);
+      const KvRsrc rn = nvfp4_rsrc(a, pgn, g, none);
+
+      // ---- S^T = K Q^T, then the next block's K
+      f32x4 sacc[8];
+#pragma unroll
+      for (int tau = 0; tau < 8; tau++) {
+        const uint32_t sc2 = fp8x2_f16x2<false>(K.ks[tau]);  // groups 2*q4, 2*q4+1
+        const uint32_t slo = bcast_lo16(sc2), shi = bcast_hi16(sc2);
+        f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int s = 0; s < 4; s++) {
+          const u32x4 kv = nvfp4x8_f16(K.kd[tau][s], s < 2 ? slo : shi);
+          acc = MT::mma(__builtin_bit_cast(vec, kv), qb[s], acc);
+        }
+        sacc[tau] = acc;
+      }
+      load_k(rn, off, K);
+
+      // ---- V scales to fp16 in LDS (wave-private)
+      {
+        const u32x4 lo = fp8x8_f16(V.vs.x, V.vs.y), hi = fp8x8_f16(V.vs.z, V.vs.w);
+        u32x4* dst = reinterpret_cast<u32x4*>(vs_stage + 16 * lane);
+        dst[0] = lo;
+        dst[1] = hi;
+        wave_lds_sync();
+      }
+
+      // ---- online softmax
+      vec pb[4];
+      softmax_block(sacc, blk, blk * kBlock + kBlock - 1 > p, pb);
+
+      // ---- O^T += V^T P^T, then the next block's V
 #pragma unroll
       for (int dt = 0; dt < 8; dt++) {
 #pragma unroll
         for (int s = 0; s < 4; s++) {
           const u32x4 sc = *reinterpret_cast<const u32x4*>(vs_stage + dt * 128 + 32 * q4 + 8 * s);
-          const u32x4 vv = nvfp4x8_f16_each(vd[dt][s], sc);
+          const u32x4 vv = nvfp4x8_f16_each(V.vd[dt][s], sc);
           st.o[dt] = MT::mma(__builtin_bit_cast(vec, vv), pb[s], st.o[dt]);
         }
       }
       wave_lds_sync();  // the stage is overwritten by the next block
-    } else {
+      load_v(rn, off, V);
+    }
+  } else {
+    for (int i = wave; i < n; i += W) {
+      const int blk = __builtin_amdgcn_readfirstlane(blist[i]);
+      const size_t pg = (size_t)__builtin_amdgcn_readfirstlane(plist[i]) * a.Hkv + g;
+      const int rho = lane & 15;
+      const uint16_t* kb = reinterpret_cast<const uint16_t*>(a.k_data) + pg * (kBlock * kHeadDim);
+      f32x4 sacc[8];
+#pragma unroll
+      for (int tau = 0; tau < 8; tau++) {
+        const u32x4* kr = reinterpret_cast<const u32x4*>(kb + kappa(tau, rho) * kHeadDim + 32 * q4);
+        f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int s = 0; s < 4; s++) acc = MT::mma(__builtin_bit_cast(vec, kr[s]), qb[s], acc);
+        sacc[tau] = acc;
+      }
+      vec pb[4];
+      softmax_block(sacc, blk, blk * kBlock + kBlock - 1 > p, pb);
       const uint16_t* vb = reinterpret_cast<const uint16_t*>(a.v_data) + pg * (kHeadDim * kBlock);
 #pragma unroll
       for (int dt = 0; dt < 8; dt++) {
@@ -349,24 +457,33 @@ __global__ __launch_bounds__(64 * W) void sparse_attn_kernel(AttnArgs a) {
   }
 }
 
+// Dynamic LDS: the pooled scores of one token (fused selection), the
+// per-wave V-scale stages, and the merge slots reuse one region.
+size_t attn_lds_bytes(const AttnArgs& a, int W) {
+  size_t sel = a.pooled ? (size_t)a.maxb * sizeof(int32_t) : 0;  // page table
+  size_t stage = (size_t)W * 1024 * 2;
+  size_t merge = (size_t)(W / 2) * kSlotFloats * 4;
+  size_t m = sel > stage ? sel : stage;
+  return m > merge ? m : merge;
+}
+
 template <bool NVFP4>
-hipError_t launch_w(const AttnArgs& a, int waves, hipStream_t s) {
+hipError_t launch_w(const AttnArgs& a, int waves, hipStream_t s, const KTimer* tm) {
   const dim3 grid(a.B * a.Tq * a.Hkv);
+  const size_t lds = attn_lds_bytes(a, waves);
   switch (waves) {
-    case 1: sparse_attn_kernel<NVFP4, 1><<<grid, 64, 0, s>>>(a); break;
-    case 2: sparse_attn_kernel<NVFP4, 2><<<grid, 128, 0, s>>>(a); break;
-    case 4: sparse_attn_kernel<NVFP4, 4><<<grid, 256, 0, s>>>(a); break;
-    case 8: sparse_attn_kernel<NVFP4, 8><<<grid, 512, 0, s>>>(a); break;
-    case 16: sparse_attn_kernel<NVFP4, 16><<<grid, 1024, 0, s>>>(a); break;
+    case 2: return launch_kernel(sparse_attn_kernel<NVFP4, 2>, grid, dim3(128), lds, s, a, tm);
+    case 4: return launch_kernel(sparse_attn_kernel<NVFP4, 4>, grid, dim3(256), lds, s, a, tm);
+    case 8: return launch_kernel(sparse_attn_kernel<NVFP4, 8>, grid, dim3(512), lds, s, a, tm);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_attn(const AttnArgs& a, bool nvfp4, int waves, hipStream_t s) {
-  return nvfp4 ? launch_w<true>(a, waves, s) : launch_w<false>(a, waves, s);
+hipError_t launch_attn(const AttnArgs& a, bool nvfp4, int waves, hipStream_t s, const KTimer* tm) {
+  if (a.top_k < 1 || a.top_k > kTopkMax || a.maxb < 1 || a.maxb > kSelectMaxBlocks) return hipErrorInvalidValue;
+  return nvfp4 ? launch_w<true>(a, waves, s, tm) : launch_w<false>(a, waves, s, tm);
 }
 
 }  // namespace msa

@@ -234,7 +234,8 @@ __global__ __launch_bounds__(256, indexer_occupancy(FP8, HP, TQ)) void indexer_p
   static_assert(S::RT <= 2, "at most 32 query rows");
   extern __shared__ int32_t prefix[];  // [B + 1]: first work block of each sequence
   __shared__ int32_t wsum[4];
-  const int tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  const int tid = threadIdx.x, lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps loop control scalar
   const uint32_t loff = ktile_lane_off<FP8>(lane);
 
   // ---- prefix sum of work blocks over the batch (each thread: a run of
@@ -371,15 +372,14 @@ int persistent_grid(const IndexerArgs& a, int occupancy, size_t lds) {
 }
 
 template <bool FP8, int HP, bool SCORES>
-hipError_t launch_hp(const IndexerArgs& a, hipStream_t s) {
+hipError_t launch_hp(const IndexerArgs& a, hipStream_t s, const KTimer* tm) {
   const size_t lds = ((size_t)a.B + 1) * sizeof(int32_t);
   switch (a.Tq) {
 #define MSA_TQ_CASE(T)                                                                                 \
   case T:                                                                                              \
     if constexpr (Shape<HP, T>::RT <= 2) {                                                             \
       const int grid = persistent_grid(a, indexer_occupancy(FP8, HP, T), lds);                         \
-      indexer_pool_kernel<FP8, HP, T, SCORES><<<grid, 256, lds, s>>>(a);                               \
-      return hipGetLastError();                                                                        \
+      return launch_kernel(indexer_pool_kernel<FP8, HP, T, SCORES>, dim3(grid), dim3(256), lds, s, a, tm); \
     }                                                                                                  \
     break;
     MSA_TQ_CASE(1)
@@ -399,15 +399,15 @@ hipError_t launch_hp(const IndexerArgs& a, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_indexer(const IndexerArgs& a, bool fp8, int hp, hipStream_t s) {
+hipError_t launch_indexer(const IndexerArgs& a, bool fp8, int hp, hipStream_t s, const KTimer* tm) {
   if ((a.scores != nullptr) == (a.pooled != nullptr)) return hipErrorInvalidValue;
   if (a.B < 1 || a.B > kIndexerMaxSeqs || a.cus < 1 || a.wgs_per_cu < 1) return hipErrorInvalidValue;
   if (a.scores) {
-    if (fp8) return hp == 8 ? launch_hp<true, 8, true>(a, s) : launch_hp<true, 4, true>(a, s);
-    return hp == 8 ? launch_hp<false, 8, true>(a, s) : launch_hp<false, 4, true>(a, s);
+    if (fp8) return hp == 8 ? launch_hp<true, 8, true>(a, s, tm) : launch_hp<true, 4, true>(a, s, tm);
+    return hp == 8 ? launch_hp<false, 8, true>(a, s, tm) : launch_hp<false, 4, true>(a, s, tm);
   }
-  if (fp8) return hp == 8 ? launch_hp<true, 8, false>(a, s) : launch_hp<true, 4, false>(a, s);
-  return hp == 8 ? launch_hp<false, 8, false>(a, s) : launch_hp<false, 4, false>(a, s);
+  if (fp8) return hp == 8 ? launch_hp<true, 8, false>(a, s, tm) : launch_hp<true, 4, false>(a, s, tm);
+  return hp == 8 ? launch_hp<false, 8, false>(a, s, tm) : launch_hp<false, 4, false>(a, s, tm);
 }
 
 }  // namespace msa

@@ -89,16 +89,15 @@ msa_status_t check_cache_idx(const msa_params_t* p, const msa_cache_t* c) {
   return MSA_OK;
 }
 
-// Workspace of msa_decode_layer: pooled scores and the selection.
+// Workspace of msa_decode_layer: the pooled block scores.
 struct Layout {
-  size_t pooled_off, sel_off, total;
+  size_t pooled_off, total;
 };
 Layout layout(const msa_params_t* p) {
   Layout L;
   const size_t bt = (size_t)p->num_seqs * p->q_len;
   L.pooled_off = 0;
-  L.sel_off = align256(bt * p->max_blocks_per_seq * sizeof(float));
-  L.total = L.sel_off + align256(bt * p->top_k * sizeof(int32_t));
+  L.total = align256(bt * p->max_blocks_per_seq * sizeof(float));
   return L;
 }
 
@@ -119,14 +118,17 @@ int device_cus() {
   return cached[dev];
 }
 
-// Waves per attention workgroup: about 2048 waves in flight, at most one
-// wave per selected block, at most 8 (16 waves of the NVFP4 kernel would
-// not fit their registers).
+// Waves per attention workgroup: 4 (two workgroups per compute unit) when
+// the batch has at least two (sequence, token, KV head) items per compute
+// unit, else 8 so that the selected blocks of the few items are spread over
+// more waves.
+#ifndef MSA_ATTN_WAVES
+#define MSA_ATTN_WAVES 0
+#endif
 int attn_waves(const msa_params_t* p) {
+  if (MSA_ATTN_WAVES > 0) return MSA_ATTN_WAVES;
   const int64_t items = (int64_t)p->num_seqs * p->q_len * p->num_kv_heads;
-  int w = 1;
-  while (w < 8 && w < p->top_k && items * w < 2048) w *= 2;
-  return w;
+  return items >= 2 * (int64_t)device_cus() ? 4 : 8;
 }
 
 IndexerArgs indexer_args(const msa_params_t* p, const msa_cache_t* c, const void* idx_q, const float* idx_w) {
@@ -153,11 +155,12 @@ float softmax_scale(const msa_params_t* p) {
   return p->softmax_scale > 0.0f ? p->softmax_scale : 1.0f / sqrtf((float)p->head_dim);
 }
 
-AttnArgs attn_args(const msa_params_t* p, const msa_cache_t* c, const void* q, const int32_t* sel, void* out,
-                   float* lse) {
+AttnArgs attn_args(const msa_params_t* p, const msa_cache_t* c, const void* q, const float* pooled, int32_t* sel,
+                   void* out, float* lse) {
   AttnArgs a;
   a.block_table = c->block_table;
   a.ctx_lens = c->ctx_lens;
+  a.pooled = pooled;
   a.sel = sel;
   a.q = static_cast<const uint16_t*>(q);
   a.k_data = static_cast<const uint8_t*>(c->k_data);
@@ -177,11 +180,18 @@ AttnArgs attn_args(const msa_params_t* p, const msa_cache_t* c, const void* q, c
   a.maxb = p->max_blocks_per_seq;
   a.num_pages = p->num_pages;
   a.top_k = p->top_k;
+  a.keep_last = p->keep_last;
   return a;
 }
 
-void record(void* const* ev, int i, hipStream_t s) {
-  if (ev && ev[i]) (void)hipEventRecord(static_cast<hipEvent_t>(ev[i]), s);
+// Start/stop events of stage i from the caller's array (2 per stage).
+KTimer stage_timer(void* const* ev, int i) {
+  KTimer t;
+  if (ev) {
+    t.start = static_cast<hipEvent_t>(ev[2 * i]);
+    t.stop = static_cast<hipEvent_t>(ev[2 * i + 1]);
+  }
+  return t;
 }
 
 }  // namespace
@@ -238,7 +248,7 @@ msa_status_t msa_sparse_attn_decode(const msa_params_t* p, const msa_cache_t* c,
   if (st != MSA_OK) return st;
   if ((st = check_cache_kv(p, c)) != MSA_OK) return st;
   if (!q || !sel || !out) return fail(MSA_ERR_INVALID_ARG, "q / sel / out is NULL");
-  AttnArgs a = attn_args(p, c, q, sel, out, lse);
+  AttnArgs a = attn_args(p, c, q, nullptr, const_cast<int32_t*>(sel), out, lse);
   hipError_t e = launch_attn(a, p->kv_dtype == MSA_KV_NVFP4, attn_waves(p), static_cast<hipStream_t>(stream));
   return e == hipSuccess ? MSA_OK : hip_fail(e, "attention launch");
 }
@@ -260,35 +270,17 @@ msa_status_t msa_decode_layer_traced(const msa_params_t* p, const msa_cache_t* c
   hipStream_t s = static_cast<hipStream_t>(stream);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   float* pooled = reinterpret_cast<float*>(ws + L.pooled_off);
-  int32_t* sel = sel_out ? sel_out : reinterpret_cast<int32_t*>(ws + L.sel_off);
 
-  record(ev, 0, s);
   IndexerArgs ia = indexer_args(p, c, idx_q, idx_w);
   ia.pooled = pooled;
-  hipError_t e = launch_indexer(ia, p->idx_dtype == MSA_IDX_FP8_E4M3, p->idx_heads <= 4 ? 4 : 8, s);
+  const KTimer t0 = stage_timer(ev, 0), t1 = stage_timer(ev, 1);
+  hipError_t e = launch_indexer(ia, p->idx_dtype == MSA_IDX_FP8_E4M3, p->idx_heads <= 4 ? 4 : 8, s, &t0);
   if (e != hipSuccess) return hip_fail(e, "indexer launch");
-  record(ev, 1, s);
 
-  SelectArgs sa;
-  sa.ctx_lens = c->ctx_lens;
-  sa.pooled_in = pooled;
-  sa.scores_in = nullptr;
-  sa.pooled_out = nullptr;
-  sa.sel = sel;
-  sa.nsel = nullptr;
-  sa.B = p->num_seqs;
-  sa.Tq = p->q_len;
-  sa.maxb = p->max_blocks_per_seq;
-  sa.top_k = p->top_k;
-  sa.keep_last = p->keep_last;
-  e = launch_select(sa, s);
-  if (e != hipSuccess) return hip_fail(e, "select launch");
-  record(ev, 2, s);
-
-  AttnArgs aa = attn_args(p, c, q, sel, out, lse);
-  e = launch_attn(aa, p->kv_dtype == MSA_KV_NVFP4, attn_waves(p), s);
+  // selection (from the pooled scores) fused into the attention kernel
+  AttnArgs aa = attn_args(p, c, q, pooled, sel_out, out, lse);
+  e = launch_attn(aa, p->kv_dtype == MSA_KV_NVFP4, attn_waves(p), s, &t1);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
-  record(ev, 3, s);
   return MSA_OK;
 }
 

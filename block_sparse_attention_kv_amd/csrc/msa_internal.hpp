@@ -1,6 +1,7 @@
 // msa_internal.hpp -- kernel argument blocks and launchers shared between the
 // kernel translation units and the C-ABI layer (msa_api.hip).
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -23,6 +24,10 @@ struct IndexerArgs {
 
 // The indexer keeps a prefix sum of blocks per sequence in LDS.
 constexpr int kIndexerMaxSeqs = 8192;
+// Selection: at most 16 blocks per query token; the pooled scores of one
+// token (at most 8192 blocks) are held in LDS.
+constexpr int kTopkMax = 16;
+constexpr int kSelectMaxBlocks = 8192;
 
 // Pool (optional) + top-k block selection per (sequence, query token).
 struct SelectArgs {
@@ -35,11 +40,16 @@ struct SelectArgs {
   int B, Tq, maxb, top_k, keep_last;
 };
 
-// Sparse attention over the selected blocks with the in-WG LSE combine.
+// Sparse attention over the selected blocks with the in-workgroup LSE
+// combine. With `pooled` set, every workgroup first selects its query
+// token's blocks from the pooled scores (fused decode layer) and the
+// workgroups of KV head 0 write the selection to `sel` if it is not null;
+// otherwise the selection is read from `sel`.
 struct AttnArgs {
   const int32_t* block_table;
   const int32_t* ctx_lens;
-  const int32_t* sel;       // [B][Tq][top_k]
+  const float* pooled;      // [B][Tq][maxb] or nullptr
+  int32_t* sel;             // [B][Tq][top_k]: input, or output when pooled
   const uint16_t* q;        // bf16 [B][Tq][Hq][128]
   const uint8_t* k_data;
   const uint8_t* k_scale;
@@ -49,12 +59,34 @@ struct AttnArgs {
   float* lse;               // [B][Tq][Hq] or nullptr
   float score_scale;        // softmax_scale * log2(e) * k_tensor_scale
   float v_scale_mul;        // v_tensor_scale
-  int B, Tq, Hq, Hkv, grp, maxb, num_pages, top_k;
+  int B, Tq, Hq, Hkv, grp, maxb, num_pages, top_k, keep_last;
 };
 
-hipError_t launch_indexer(const IndexerArgs& a, bool fp8, int hp, hipStream_t s);
+// Kernel timing hook: when either event is set, the kernel is dispatched with
+// hipExtLaunchKernel, which records the kernel's own start and end into them
+// (no extra packets in the queue between kernels).
+struct KTimer {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+
+// Launch of a kernel taking one argument block by value.
+template <typename Args>
+hipError_t launch_kernel(void (*kern)(Args), dim3 grid, dim3 block, size_t lds, hipStream_t s, const Args& a,
+                         const KTimer* t) {
+  if (t && (t->start || t->stop)) {
+    Args copy = a;
+    void* args[] = {&copy};
+    const hipError_t e = hipExtLaunchKernel(reinterpret_cast<const void*>(kern), grid, block, args, lds, s,
+                                            t->start, t->stop, 0);
+    return e != hipSuccess ? e : hipGetLastError();
+  }
+  kern<<<grid, block, lds, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_indexer(const IndexerArgs& a, bool fp8, int hp, hipStream_t s, const KTimer* t = nullptr);
 hipError_t launch_select(const SelectArgs& a, hipStream_t s);
-hipError_t launch_attn(const AttnArgs& a, bool nvfp4, int waves, hipStream_t s);
+hipError_t launch_attn(const AttnArgs& a, bool nvfp4, int waves, hipStream_t s, const KTimer* t = nullptr);
 hipError_t launch_debug_nvfp4(const uint8_t* codes, const uint8_t* scales, int64_t n_groups,
                               float* out, hipStream_t s);
 hipError_t launch_debug_fp8(const uint8_t* codes, int64_t n, float* out, hipStream_t s);

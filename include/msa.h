@@ -103,7 +103,7 @@ extern "C" {
 #define MSA_MAX_BLOCKS 8192  /* max_blocks_per_seq limit (1,048,576 tokens) */
 #define MSA_MAX_GROUP 16     /* num_q_heads / num_kv_heads limit */
 #define MSA_MAX_SEQS 8192    /* num_seqs limit */
-#define MSA_NUM_STAGES 3     /* kernels enqueued by msa_decode_layer */
+#define MSA_NUM_STAGES 2     /* kernels enqueued by msa_decode_layer */
 
 typedef enum {
   MSA_OK = 0,
@@ -201,8 +201,11 @@ msa_status_t msa_sparse_attn_decode(const msa_params_t* p, const msa_cache_t* ca
                                     float* lse, void* workspace, size_t ws_bytes,
                                     void* stream);
 
-/* The whole decode step of one MSA layer: indexer + pool, select, sparse
- * attention, in MSA_NUM_STAGES kernels on `stream`.
+/* The whole decode step of one MSA layer in MSA_NUM_STAGES kernels on
+ * `stream`: (1) indexer + per-block max pool into the workspace, (2) per
+ * (sequence, query token, KV head): selection from the pooled scores, then
+ * sparse attention. The selection equals msa_pool_select_blocks' on the
+ * same pooled scores.
  *   sel_out device i32[B][q_len][top_k] or NULL: the selection used.
  *   lse     as in msa_sparse_attn_decode, or NULL.
  *   workspace at least msa_workspace_size(p) bytes of device memory, 256-byte
@@ -213,9 +216,11 @@ msa_status_t msa_decode_layer(const msa_params_t* p, const msa_cache_t* cache,
                               void* workspace, size_t ws_bytes, void* stream);
 
 /* msa_decode_layer with a tracing hook: when `stage_events` is not NULL it
- * holds MSA_NUM_STAGES + 1 hipEvent_t handles (created by the caller); event
- * i is recorded on `stream` before stage i is enqueued and the last one after
- * the last stage, so the caller can time each kernel with hipEventElapsedTime. */
+ * holds 2 * MSA_NUM_STAGES hipEvent_t handles (created by the caller, NULL
+ * entries allowed). Kernel i is dispatched so that the dispatch itself
+ * records the kernel's start into event 2i and its end into event 2i+1
+ * (hipExtLaunchKernel), without extra packets between the kernels; the caller
+ * times kernel i with hipEventElapsedTime(event 2i, event 2i+1). */
 msa_status_t msa_decode_layer_traced(const msa_params_t* p, const msa_cache_t* cache,
                                      const void* q, const void* idx_q, const float* idx_w,
                                      void* out, float* lse, int32_t* sel_out,

@@ -127,3 +127,26 @@ def test_config1_full():
 def test_config2_full():
     ties, mx, mean = G.layer_parity(make_config(2), strict=True)
     print("cfg2: ties %d max-abs %.2e mean-abs %.2e" % (ties, mx, mean))
+
+
+def test_decode_layer_traced_matches_plain():
+    # the tracing entry point (kernels dispatched with start/stop events)
+    # computes exactly what the plain one does, and every event pair spans a
+    # positive kernel duration
+    w = small_cases()[2]
+    run = G.Run(w)
+    plain = run.layer()
+    prm = w.params
+    B, Tq, Hq, K = prm["num_seqs"], prm["q_len"], prm["num_q_heads"], prm["top_k"]
+    out = torch.empty((B, Tq, Hq, 128), dtype=torch.int16, device="cuda")
+    lse = torch.empty((B, Tq, Hq), dtype=torch.float32, device="cuda")
+    sel = torch.empty((B, Tq, K), dtype=torch.int32, device="cuda")
+    ws = msa.alloc_workspace(run.params, "cuda")
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * msa.NUM_STAGES)]
+    msa.msa_decode_layer(run.params, run.cache, run.q, run.idx_q, run.idx_w, out, ws, lse=lse, sel_out=sel,
+                         stage_events=evs)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy(), plain["out_bits"])
+    assert np.array_equal(sel.cpu().numpy(), plain["sel"])
+    for i in range(msa.NUM_STAGES):
+        assert evs[2 * i].elapsed_time(evs[2 * i + 1]) > 0.0

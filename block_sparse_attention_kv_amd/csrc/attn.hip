@@ -259,25 +259,9 @@ __global__ __launch_bounds__(64 * W, (W <= 4 ? 2 : 1)) void sparse_attn_kernel(A
   for (int d = 0; d < 8; d++) st.o[d] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
   // raw scores of one block (S^T tiles) -> online softmax update and the P^T
-  // operand; `partial`: the block holds keys past p. cscale >= 0, so the max
-  // of the scaled scores is cscale times the max of the raw ones.
-  auto softmax_block = [&](f32x4 (&sacc)[8], int blk, bool partial, vec (&pb)[4]) {
-    float rmax = -INFINITY;
-    if (partial) {
-#pragma unroll
-      for (int tau = 0; tau < 8; tau++)
-#pragma unroll
-        for (int r = 0; r < 4; r++) {
-          const bool vis = blk * kBlock + kappa(tau, 4 * q4 + r) <= p;
-          sacc[tau][r] = vis ? sacc[tau][r] : -INFINITY;
-          rmax = fmaxf(rmax, sacc[tau][r]);
-        }
-    } else {
-#pragma unroll
-      for (int tau = 0; tau < 8; tau++)
-#pragma unroll
-        for (int r = 0; r < 4; r++) rmax = fmaxf(rmax, sacc[tau][r]);
-    }
+  // operand. cscale >= 0, so the max of the scaled scores is cscale times the
+  // max of the raw ones.
+  auto softmax_update = [&](f32x4 (&sacc)[8], float rmax, bool masked, vec (&pb)[4]) {
     rmax = fmaxf(rmax, shfl_xor(rmax, 16));
     rmax = fmaxf(rmax, shfl_xor(rmax, 32));
     const float bmax = rmax == -INFINITY ? -INFINITY : rmax * cscale;
@@ -290,7 +274,7 @@ __global__ __launch_bounds__(64 * W, (W <= 4 ? 2 : 1)) void sparse_attn_kernel(A
       for (int e = 0; e < 8; e++) {
         const float x = sacc[2 * s + (e >> 2)][e & 3];
         float v = fast_exp2(fmaf(x, cscale, -mnew));
-        if (partial) v = x == -INFINITY ? 0.0f : v;
+        if (masked) v = x == -INFINITY ? 0.0f : v;
         pv[e] = v;
         psum += v;
       }
@@ -311,6 +295,30 @@ __global__ __launch_bounds__(64 * W, (W <= 4 ? 2 : 1)) void sparse_attn_kernel(A
     st.l += psum;
     st.m = mnew;
   };
+  // The block holding keys past p (the context's last block) takes the masked
+  // path; the two paths are whole branches so that full blocks do not pay for
+  // the mask.
+  auto softmax_block = [&](f32x4 (&sacc)[8], int blk, bool partial, vec (&pb)[4]) {
+    if (partial) {
+      float rmax = -INFINITY;
+#pragma unroll
+      for (int tau = 0; tau < 8; tau++)
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+          const bool vis = blk * kBlock + kappa(tau, 4 * q4 + r) <= p;
+          sacc[tau][r] = vis ? sacc[tau][r] : -INFINITY;
+          rmax = fmaxf(rmax, sacc[tau][r]);
+        }
+      softmax_update(sacc, rmax, true, pb);
+    } else {
+      float rmax = -INFINITY;
+#pragma unroll
+      for (int tau = 0; tau < 8; tau++)
+#pragma unroll
+        for (int r = 0; r < 4; r++) rmax = fmaxf(rmax, sacc[tau][r]);
+      softmax_update(sacc, rmax, false, pb);
+    }
+  };
 
   if constexpr (NVFP4) {
     // fp16 V scales of the current block: [8 groups][128 keys] per wave
@@ -330,8 +338,16 @@ __global__ __launch_bounds__(64 * W, (W <= 4 ? 2 : 1)) void sparse_attn_kernel(A
       load_k(r0, off, K);
       load_v(r0, off, V);
     }
-    for (int i = wave; i < n; i += W) {
-      const int blk = __builtin_amdgcn_readfirstlane(blist[i]);
+    // Fully unrolled over the wave's at most kTopkMax / W blocks: straight-line
+    // code keeps the compiler's load counters exact across blocks (a loop
+    // header merges the first and later iterations' load orders and makes
+    // every block wait for all outstanding loads). Iterations past the wave's
+    // last block run on empty resources and skip the softmax and P.V.
+#pragma unroll
+    for (int it = 0; it < kTopkMax / W; it++) {
+      const int i = wave + it * W;
+      const bool valid = i < n;
+      const int blk = valid ? __builtin_amdgcn_readfirstlane(blist[i]) : 0;
       const bool none = i + W >= n;
       const int pgn = none ? 0 : __builtin_amdgcn_readfirstlane(plist[i + W]);
       const KvRsrc rn = nvfp4_rsrc(a, pgn, g, none);
@@ -350,33 +366,45 @@ __global__ __launch_bounds__(64 * W, (W <= 4 ? 2 : 1)) void sparse_attn_kernel(A
         }
         sacc[tau] = acc;
       }
-      load_k(rn, off, K);
+      if (it + 1 < kTopkMax / W) load_k(rn, off, K);
 
-      // ---- V scales to fp16 in LDS (wave-private)
-      {
-        const u32x4 lo = fp8x8_f16(V.vs.x, V.vs.y), hi = fp8x8_f16(V.vs.z, V.vs.w);
-        u32x4* dst = reinterpret_cast<u32x4*>(vs_stage + 16 * lane);
-        dst[0] = lo;
-        dst[1] = hi;
-        wave_lds_sync();
-      }
-
-      // ---- online softmax
-      vec pb[4];
-      softmax_block(sacc, blk, blk * kBlock + kBlock - 1 > p, pb);
-
-      // ---- O^T += V^T P^T, then the next block's V
-#pragma unroll
-      for (int dt = 0; dt < 8; dt++) {
-#pragma unroll
-        for (int s = 0; s < 4; s++) {
-          const u32x4 sc = *reinterpret_cast<const u32x4*>(vs_stage + dt * 128 + 32 * q4 + 8 * s);
-          const u32x4 vv = nvfp4x8_f16_each(V.vd[dt][s], sc);
-          st.o[dt] = MT::mma(__builtin_bit_cast(vec, vv), pb[s], st.o[dt]);
+      if (valid) {
+        // ---- V scales to fp16 in LDS (wave-private)
+        {
+          const u32x4 lo = fp8x8_f16(V.vs.x, V.vs.y), hi = fp8x8_f16(V.vs.z, V.vs.w);
+          u32x4* dst = reinterpret_cast<u32x4*>(vs_stage + 16 * lane);
+          dst[0] = lo;
+          dst[1] = hi;
+          wave_lds_sync();
         }
+
+        // ---- online softmax
+        vec pb[4];
+        softmax_block(sacc, blk, blk * kBlock + kBlock - 1 > p, pb);
+
+        // ---- O^T += V^T P^T; the scales of dim tile dt+1 are read while
+        // tile dt is decoded and multiplied
+        u32x4 sc[4], scn[4];
+#pragma unroll
+        for (int s = 0; s < 4; s++) sc[s] = *reinterpret_cast<const u32x4*>(vs_stage + 32 * q4 + 8 * s);
+#pragma unroll
+        for (int dt = 0; dt < 8; dt++) {
+          if (dt + 1 < 8) {
+#pragma unroll
+            for (int s = 0; s < 4; s++)
+              scn[s] = *reinterpret_cast<const u32x4*>(vs_stage + (dt + 1) * 128 + 32 * q4 + 8 * s);
+          }
+#pragma unroll
+          for (int s = 0; s < 4; s++) {
+            const u32x4 vv = nvfp4x8_f16_each(V.vd[dt][s], sc[s]);
+            st.o[dt] = MT::mma(__builtin_bit_cast(vec, vv), pb[s], st.o[dt]);
+          }
+#pragma unroll
+          for (int s = 0; s < 4; s++) sc[s] = scn[s];
+        }
+        wave_lds_sync();  // the stage is overwritten by the next block
       }
-      wave_lds_sync();  // the stage is overwritten by the next block
-      load_v(rn, off, V);
+      if (it + 1 < kTopkMax / W) load_v(rn, off, V);
     }
   } else {
     for (int i = wave; i < n; i += W) {
@@ -472,7 +500,6 @@ hipError_t launch_w(const AttnArgs& a, int waves, hipStream_t s, const KTimer* t
   const dim3 grid(a.B * a.Tq * a.Hkv);
   const size_t lds = attn_lds_bytes(a, waves);
   switch (waves) {
-    case 2: return launch_kernel(sparse_attn_kernel<NVFP4, 2>, grid, dim3(128), lds, s, a, tm);
     case 4: return launch_kernel(sparse_attn_kernel<NVFP4, 4>, grid, dim3(256), lds, s, a, tm);
     case 8: return launch_kernel(sparse_attn_kernel<NVFP4, 8>, grid, dim3(512), lds, s, a, tm);
     default: return hipErrorInvalidValue;

@@ -75,6 +75,10 @@ struct MfmaT<true> {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
   }
   static __device__ __forceinline__ uint32_t pack(float x, float y) { return f32x2_to_f16x2(x, y); }
+  // acc + both halves of a packed pair (v_dot2_f32_f16 against ones)
+  static __device__ __forceinline__ float sum2(uint32_t p, float acc) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, p), f16x2{(f16)1.0f, (f16)1.0f}, acc, false);
+  }
 };
 template <>
 struct MfmaT<false> {
@@ -83,6 +87,9 @@ struct MfmaT<false> {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
   }
   static __device__ __forceinline__ uint32_t pack(float x, float y) { return f32x2_to_bf16x2(x, y); }
+  static __device__ __forceinline__ float sum2(uint32_t p, float acc) {
+    return acc + bf16_bits_to_f32(p & 0xFFFFu) + bf16_bits_to_f32(p >> 16);
+  }
 };
 
 struct SoftmaxState {
@@ -245,9 +252,12 @@ __global__ __launch_bounds__(64 * W, (W <= 4 ? 2 : 1)) void sparse_attn_kernel(A
       qb[s] = __builtin_bit_cast(vec, v);
     }
   } else {
-    cscale = a.score_scale;
+    // bf16 Q is used as is; a negative score scale (negative K tensor scale)
+    // flips Q's sign bits so that the softmax sees a scale >= 0
+    const uint32_t flip = a.score_scale < 0.0f ? 0x80008000u : 0u;
+    cscale = fabsf(a.score_scale);
 #pragma unroll
-    for (int s = 0; s < 4; s++) qb[s] = __builtin_bit_cast(vec, qraw[s]);
+    for (int s = 0; s < 4; s++) qb[s] = __builtin_bit_cast(vec, qraw[s] ^ flip);
   }
   __syncthreads();
   const int n = __builtin_amdgcn_readfirstlane(nlist);
@@ -276,7 +286,6 @@ __global__ __launch_bounds__(64 * W, (W <= 4 ? 2 : 1)) void sparse_attn_kernel(A
         float v = fast_exp2(fmaf(x, cscale, -mnew));
         if (masked) v = x == -INFINITY ? 0.0f : v;
         pv[e] = v;
-        psum += v;
       }
       u32x4 pk;
       pk.x = MT::pack(pv[0], pv[1]);
@@ -284,6 +293,9 @@ __global__ __launch_bounds__(64 * W, (W <= 4 ? 2 : 1)) void sparse_attn_kernel(A
       pk.z = MT::pack(pv[4], pv[5]);
       pk.w = MT::pack(pv[6], pv[7]);
       pb[s] = __builtin_bit_cast(vec, pk);
+      // the row sum takes the same rounded P that multiplies V
+#pragma unroll
+      for (int e = 0; e < 4; e++) psum = MT::sum2(pk[e], psum);
     }
     // rescale the running state only if some head's max grew
     if (__ballot(mnew != st.m) != 0) {

@@ -46,12 +46,51 @@ __device__ __forceinline__ int count_ge(const uint64_t (&k)[NK], uint64_t c) {
   return n;
 }
 
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) v = max(v, (uint32_t)shfl_xor((int)v, m));
+  return v;
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) v = min(v, (uint32_t)shfl_xor((int)v, m));
+  return v;
+}
+
 // Threshold T with exactly K keys >= T, K <= number of nonzero keys (keys
 // are unique). Returns T (uniform).
+//
+// The search starts below the bits that all nonzero, non-forced keys share
+// (the common prefix of their largest and smallest high words): a candidate
+// with any higher bit changed would exceed every such key, leaving at most
+// the one forced key above it, fewer than K >= 2. With K = 1, or with no
+// such key, the search covers all 64 bits.
 template <int NK>
 __device__ __forceinline__ uint64_t kth_threshold(const uint64_t (&k)[NK], int K) {
+  uint32_t hmax = 0u, hmin = 0xFFFFFFFFu;
+#pragma unroll
+  for (int j = 0; j < NK; j++) {
+    const uint32_t hi = (uint32_t)(k[j] >> 32);
+    const bool use = k[j] != 0ull && hi != 0xFFFFFFFFu;
+    hmax = use ? max(hmax, hi) : hmax;
+    hmin = use ? min(hmin, hi) : hmin;
+  }
+  hmax = wave_max_u32(hmax);
+  hmin = wave_min_u32(hmin);
   uint64_t T = 0;
-  for (int bit = 63; bit >= 0; bit--) {
+  int top = 63;
+  if (K >= 2 && hmin <= hmax) {
+    const uint32_t d = hmax ^ hmin;
+    if (d != 0u) {
+      const int b = 31 - __builtin_clz(d);
+      T = (uint64_t)(b == 31 ? 0u : (hmax >> (b + 1)) << (b + 1)) << 32;
+      top = 32 + b;
+    } else {
+      T = (uint64_t)hmax << 32;
+      top = 31;
+    }
+  }
+  for (int bit = top; bit >= 0; bit--) {
     const uint64_t cand = T | (1ull << bit);
     const int c = count_ge<NK>(k, cand);
     if (c >= K) {
@@ -129,8 +168,12 @@ __device__ int block_topk(ScoreFn score, PageFn page, int32_t* pages, int n, int
     k[4] = carry;
     const int have = nc + min(256, hi - base);
     const int K = min(top_k, have);
-    const uint64_t T = kth_threshold<5>(k, K);
-    compact_ge<5>(k, T, s.win[wave]);
+    if (base == lo) {  // first chunk: no winners carried yet
+      const uint64_t (&k4)[4] = reinterpret_cast<const uint64_t (&)[4]>(k);
+      compact_ge<4>(k4, kth_threshold<4>(k4, K), s.win[wave]);
+    } else {
+      compact_ge<5>(k, kth_threshold<5>(k, K), s.win[wave]);
+    }
     wave_lds_sync();
     nc = K;
     carry = lane < nc ? s.win[wave][lane] : 0ull;
@@ -145,10 +188,11 @@ __device__ int block_topk(ScoreFn score, PageFn page, int32_t* pages, int n, int
   __syncthreads();
   // ---- wave 0: top_k of all waves' winners (at most 16 x 16), then sort
   if (wave == 0) {
-    uint64_t k[4];
+    constexpr int NJ = (NW * kTopkCap + 63) / 64;  // key slots per lane
+    uint64_t k[NJ];
     int have = 0;
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
+    for (int j = 0; j < NJ; j++) {
       const int slot = 64 * j + lane;  // wave slot/16, entry slot%16
       const int w = slot / kTopkCap, e = slot % kTopkCap;
       k[j] = (w < NW && e < s.nwin[w]) ? s.win[w][e] : 0ull;
@@ -156,8 +200,8 @@ __device__ int block_topk(ScoreFn score, PageFn page, int32_t* pages, int n, int
 #pragma unroll
     for (int w = 0; w < NW; w++) have += s.nwin[w];
     const int K = min(top_k, have);
-    const uint64_t T = kth_threshold<4>(k, K);
-    compact_ge<4>(k, T, s.fin);
+    const uint64_t T = kth_threshold<NJ>(k, K);
+    compact_ge<NJ>(k, T, s.fin);
     wave_lds_sync();
     if (lane < K) {
       const int mine = (int)(0xFFFFFFFFu - (uint32_t)s.fin[lane]);

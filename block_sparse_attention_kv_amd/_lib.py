@@ -78,6 +78,7 @@ def load():
         "msa_sparse_attn_decode": (st, [P, C, vp, vp, vp, vp, vp, sz, vp]),
         "msa_decode_layer": (st, [P, C, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
         "msa_decode_layer_traced": (st, [P, C, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp]),
+        "msa_kv_insert": (st, [P, C, vp, vp, vp, vp]),
         "msa_debug_dequant_nvfp4": (st, [vp, vp, i64, vp, vp]),
         "msa_debug_dequant_fp8": (st, [vp, i64, vp, vp]),
         "msa_status_string": (ctypes.c_char_p, [st]),
@@ -93,7 +94,8 @@ def load():
 
 
 EXPORTED = ("msa_workspace_size", "msa_indexer_scores", "msa_pool_select_blocks", "msa_sparse_attn_decode",
-            "msa_decode_layer", "msa_decode_layer_traced", "msa_debug_dequant_nvfp4", "msa_debug_dequant_fp8",
+            "msa_decode_layer", "msa_decode_layer_traced", "msa_kv_insert", "msa_debug_dequant_nvfp4",
+            "msa_debug_dequant_fp8",
             "msa_status_string", "msa_last_error", "msa_version")
 
 
@@ -211,6 +213,15 @@ def msa_decode_layer(params, cache, q, idx_q, idx_w, out, workspace, lse=None, s
                                        _ptr(out), _ptr(lse), _ptr(sel_out), _ptr(workspace), ws_bytes,
                                        _stream(stream), arr)
     _check(st, "msa_decode_layer")
+
+
+def msa_kv_insert(params, cache, new_k, new_v, new_idx_k, stream=None):
+    """Quantise the q_len new tokens (bf16 [B][q_len][num_kv_heads][128] K and
+    V, bf16 [B][q_len][64] indexer keys) into the paged cache in place."""
+    L = load()
+    c = cache.c()
+    _check(L.msa_kv_insert(ctypes.byref(params), ctypes.byref(c), _ptr(new_k), _ptr(new_v), _ptr(new_idx_k),
+                           _stream(stream)), "msa_kv_insert")
 
 
 def msa_debug_dequant_nvfp4(codes, scales, out, stream=None):

@@ -290,6 +290,56 @@ msa_status_t msa_decode_layer(const msa_params_t* p, const msa_cache_t* c, const
   return msa_decode_layer_traced(p, c, q, idx_q, idx_w, out, lse, sel_out, workspace, ws_bytes, stream, nullptr);
 }
 
+msa_status_t msa_kv_insert(const msa_params_t* p, const msa_cache_t* c, const void* new_k, const void* new_v,
+                           const void* new_idx_k, void* stream) {
+  g_err[0] = 0;
+  if (!p) return fail(MSA_ERR_INVALID_ARG, "params is NULL");
+  if (p->num_seqs < 1 || p->q_len < 1 || p->num_kv_heads < 1 || p->max_blocks_per_seq < 1 || p->num_pages < 1)
+    return fail(MSA_ERR_INVALID_ARG, "sizes must be positive (B=%d Tq=%d Hkv=%d maxb=%d pages=%d)", p->num_seqs,
+                p->q_len, p->num_kv_heads, p->max_blocks_per_seq, p->num_pages);
+  if (p->head_dim != MSA_HEAD_DIM) return fail(MSA_ERR_UNSUPPORTED, "head_dim %d (only 128)", p->head_dim);
+  if (p->idx_dim != MSA_IDX_DIM) return fail(MSA_ERR_UNSUPPORTED, "idx_dim %d (only 64)", p->idx_dim);
+  if (p->block_size != MSA_BLOCK_SIZE) return fail(MSA_ERR_UNSUPPORTED, "block_size %d (only 128)", p->block_size);
+  if (p->max_blocks_per_seq > MSA_MAX_BLOCKS)
+    return fail(MSA_ERR_UNSUPPORTED, "max_blocks_per_seq %d > %d", p->max_blocks_per_seq, MSA_MAX_BLOCKS);
+  if (p->kv_dtype != MSA_KV_BF16 && p->kv_dtype != MSA_KV_NVFP4)
+    return fail(MSA_ERR_UNSUPPORTED, "kv_dtype %d", p->kv_dtype);
+  if (p->idx_dtype != MSA_IDX_BF16 && p->idx_dtype != MSA_IDX_FP8_E4M3)
+    return fail(MSA_ERR_UNSUPPORTED, "idx_dtype %d", p->idx_dtype);
+  if ((int64_t)p->q_len > (int64_t)65535 * 64) return fail(MSA_ERR_UNSUPPORTED, "q_len %d too large", p->q_len);
+  if ((int64_t)p->num_seqs * (p->num_kv_heads + 1) > 0x7FFFFFFF)
+    return fail(MSA_ERR_UNSUPPORTED, "too many (sequence, head) items");
+  msa_status_t st;
+  if ((st = check_cache_kv(p, c)) != MSA_OK) return st;
+  if ((st = check_cache_idx(p, c)) != MSA_OK) return st;
+  if (p->kv_dtype == MSA_KV_NVFP4 && (c->k_tensor_scale == 0.0f || c->v_tensor_scale == 0.0f))
+    return fail(MSA_ERR_INVALID_ARG, "tensor scales must be nonzero");
+  if (!new_k || !new_v || !new_idx_k) return fail(MSA_ERR_INVALID_ARG, "new_k / new_v / new_idx_k is NULL");
+  InsertArgs a;
+  a.block_table = c->block_table;
+  a.ctx_lens = c->ctx_lens;
+  a.k_data = static_cast<uint8_t*>(const_cast<void*>(c->k_data));
+  a.k_scale = static_cast<uint8_t*>(const_cast<void*>(c->k_scale));
+  a.v_data = static_cast<uint8_t*>(const_cast<void*>(c->v_data));
+  a.v_scale = static_cast<uint8_t*>(const_cast<void*>(c->v_scale));
+  a.idx_k = static_cast<uint8_t*>(const_cast<void*>(c->idx_k));
+  a.idx_k_scale = const_cast<float*>(c->idx_k_scale);
+  a.new_k = static_cast<const uint16_t*>(new_k);
+  a.new_v = static_cast<const uint16_t*>(new_v);
+  a.new_idx_k = static_cast<const uint16_t*>(new_idx_k);
+  a.k_ts = (double)c->k_tensor_scale;
+  a.v_ts = (double)c->v_tensor_scale;
+  a.B = p->num_seqs;
+  a.Tq = p->q_len;
+  a.Hkv = p->num_kv_heads;
+  a.maxb = p->max_blocks_per_seq;
+  a.num_pages = p->num_pages;
+  a.nvfp4 = p->kv_dtype == MSA_KV_NVFP4;
+  a.idx_fp8 = p->idx_dtype == MSA_IDX_FP8_E4M3;
+  hipError_t e = launch_insert(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MSA_OK : hip_fail(e, "insert launch");
+}
+
 msa_status_t msa_debug_dequant_nvfp4(const uint8_t* codes, const uint8_t* scales, int64_t n_groups, float* out,
                                      void* stream) {
   g_err[0] = 0;

@@ -62,6 +62,25 @@ struct AttnArgs {
   int B, Tq, Hq, Hkv, grp, maxb, num_pages, top_k, keep_last;
 };
 
+// KV-insert of the new tokens into the paged caches (writes through the
+// cache pointers).
+struct InsertArgs {
+  const int32_t* block_table;  // [B][maxb]
+  const int32_t* ctx_lens;     // [B]
+  uint8_t* k_data;             // NVFP4 u8[P][G][128][64] or bf16 [P][G][128][128]
+  uint8_t* k_scale;            // u8[P][G][128][8] (NVFP4)
+  uint8_t* v_data;             // NVFP4 u8[P][G][128 d][64] or bf16 [P][G][128 d][128]
+  uint8_t* v_scale;            // u8[P][G][8][128] (NVFP4)
+  uint8_t* idx_k;              // FP8 u8[P][128][64] or bf16 [P][128][64]
+  float* idx_k_scale;          // [P][128] (FP8)
+  const uint16_t* new_k;       // bf16 [B][Tq][G][128]
+  const uint16_t* new_v;       // bf16 [B][Tq][G][128]
+  const uint16_t* new_idx_k;   // bf16 [B][Tq][64]
+  double k_ts, v_ts;           // tensor scales (NVFP4)
+  int B, Tq, Hkv, maxb, num_pages;
+  int nvfp4, idx_fp8;
+};
+
 // Kernel timing hook: when either event is set, the kernel is dispatched with
 // hipExtLaunchKernel, which records the kernel's own start and end into them
 // (no extra packets in the queue between kernels).
@@ -86,6 +105,7 @@ hipError_t launch_kernel(void (*kern)(Args), dim3 grid, dim3 block, size_t lds, 
 
 hipError_t launch_indexer(const IndexerArgs& a, bool fp8, int hp, hipStream_t s, const KTimer* t = nullptr);
 hipError_t launch_select(const SelectArgs& a, hipStream_t s);
+hipError_t launch_insert(const InsertArgs& a, hipStream_t s);
 hipError_t launch_attn(const AttnArgs& a, bool nvfp4, int waves, hipStream_t s, const KTimer* t = nullptr);
 hipError_t launch_debug_nvfp4(const uint8_t* codes, const uint8_t* scales, int64_t n_groups,
                               float* out, hipStream_t s);

@@ -227,6 +227,35 @@ msa_status_t msa_decode_layer_traced(const msa_params_t* p, const msa_cache_t* c
                                      void* workspace, size_t ws_bytes, void* stream,
                                      void* const* stage_events);
 
+/* KV-insert: quantise the q_len new tokens of every sequence and write them
+ * into the paged caches -- the step that precedes the decode of those tokens
+ * [ainewsbites page "vLLM Adds Day-0 Support for MiniMax-M3.1-Flash on NVIDIA
+ * and AMD GPUs": section "A model built for efficient inference", the model
+ * is trained for an NVFP4 KV cache; section "Kernel and serving
+ * optimizations", KV-insert is fused with the kernels that produce K and V].
+ * Token t of sequence b goes to position pos = ctx_lens[b] - q_len + t
+ * (ctx_lens counts the new tokens, as in the decode calls): page
+ * block_table[b][pos / 128], slot pos % 128. Nothing else is written; a V
+ * byte shared with an older token keeps that token's nibble.
+ *   new_k, new_v  device bf16[B][q_len][num_kv_heads][128]
+ *   new_idx_k     device bf16[B][q_len][64]
+ * NVFP4 K/V, per token, KV head and 16-element group (IEEE double, in this
+ * order): y = x / tensor_scale; scale code = E4M3(max|y| / 6); code =
+ * E2M1(y / decoded scale), or +0 when the scale is 0. E4M3 and E2M1 round to
+ * the nearest value, ties to the even code, saturating at 448 and 6; a value
+ * that rounds to zero is stored as +0.
+ * FP8 indexer keys, per token: s = max|k| / 448 rounded to fp32 (1.0 when
+ * the max is 0); byte = E4M3(k / s) (double quotient), idx_k_scale = s.
+ * bf16 caches store the values unchanged.
+ * The cache buffers are written through the pointers of msa_cache_t (their
+ * const qualifies the decode calls only). Tokens with pos < 0 or pos >=
+ * max_blocks_per_seq*128, or whose page is outside [0, num_pages), are
+ * skipped. The written slots of different sequences must not share a page
+ * slot. NaN and infinite inputs are not supported. */
+msa_status_t msa_kv_insert(const msa_params_t* p, const msa_cache_t* cache,
+                           const void* new_k, const void* new_v,
+                           const void* new_idx_k, void* stream);
+
 /* Debug exports: run the kernels' own dequantisation helpers over a flat
  * buffer, for bit-exact tests of the decoders.
  *   msa_debug_dequant_nvfp4: codes device u8[n_groups*8] (16 elements per

@@ -25,6 +25,12 @@ only, the most recent block is always kept, so at most 2,048 keys per query]:
  6. attend   o = softmax(scale * q K^T) V over the visible keys of the
              selected blocks, lse = log sum exp(scale * q K^T)  (exact)
 
+Before the decode, kv_insert (section 0) writes new tokens into the caches:
+the NVFP4 quantiser (E4M3 scale of max|y|/6 per 16 elements, E2M1 codes)
+and the FP8 indexer-key quantiser (per-token scale max|k|/448), each
+rounding to the nearest representable value with ties to the even code
+[same page, section "Kernel and serving optimizations": the KV-insert step].
+
 The readings (c1..c17) are listed, with their reasons, in the design notes of
 the repository. Every function below is pinned by CPU tests to something
 other than itself: exhaustive decoder tables against torch's float8 cast and
@@ -266,6 +272,110 @@ def attend_token(w, b, t, blocks, p_t=None):
         K, V = gather_selected(w, b, blocks, g, p_t)
         o[g * grp:(g + 1) * grp], lse[g * grp:(g + 1) * grp] = attend(q[g * grp:(g + 1) * grp], K, V, sc)
     return o, lse
+
+
+# ------------------------------------------------------- 0. KV-insert
+
+def _nearest_code(a, table):
+    """Index of the value of `table` (ascending, non-negative) nearest to each
+    a >= 0; a tie between two neighbours goes to the even index (the even
+    code: the mantissa's last bit is the code's last bit). Values above the
+    table's end go to its last entry (saturation)."""
+    a = np.asarray(a, dtype=np.float64)
+    n = table.shape[0]
+    hi = np.clip(np.searchsorted(table, a, side="left"), 0, n - 1)
+    lo = np.clip(hi - 1, 0, n - 1)
+    dlo, dhi = np.abs(a - table[lo]), np.abs(table[hi] - a)
+    return np.where(dlo < dhi, lo, np.where(dhi < dlo, hi, np.where(lo % 2 == 0, lo, hi)))
+
+
+def e4m3_encode(x):
+    """float64 -> OCP E4M3 bytes: the nearest finite E4M3 value, ties to the
+    even code, saturating at +-448; a value that rounds to zero is +0."""
+    x = np.asarray(x, dtype=np.float64)
+    mags = e4m3_to_f64(np.arange(0x7F, dtype=np.uint8))    # codes 0..0x7E, ascending
+    c = _nearest_code(np.abs(x), mags).astype(np.uint8)
+    return np.where((x < 0) & (c != 0), c | 0x80, c).astype(np.uint8)
+
+
+def e2m1_encode(x):
+    """float64 -> 4-bit E2M1 codes: the nearest of 0, .5, 1, 1.5, 2, 3, 4, 6,
+    ties to the even code, saturating at +-6; a value that rounds to zero is
+    +0."""
+    x = np.asarray(x, dtype=np.float64)
+    mags = e2m1_to_f64(np.arange(8))
+    c = _nearest_code(np.abs(x), mags).astype(np.int64)
+    return np.where((x < 0) & (c != 0), c | 8, c)
+
+
+def nvfp4_quantize_group(y):
+    """16 values (already divided by the tensor scale) -> (E4M3 scale code,
+    16 E2M1 codes): scale = E4M3(max|y| / 6), codes = E2M1(y / scale),
+    all +0 when the scale is 0 (the NVFP4 storage the decode reads: one E4M3
+    scale per 16 elements, the largest magnitude mapped to E2M1's 6)."""
+    y = np.asarray(y, dtype=np.float64)
+    sc = int(e4m3_encode(np.max(np.abs(y)) / 6.0))
+    s = float(e4m3_to_f64(np.uint8(sc)))
+    codes = e2m1_encode(y / s) if s > 0 else np.zeros(y.shape[0], dtype=np.int64)
+    return sc, codes
+
+
+def kv_insert(w, new_k, new_v, new_idx_k):
+    """Write the q_len new tokens into copies of the caches of workload `w`
+    and return them as a dict (k_data, k_scale, v_data, v_scale, idx_k,
+    idx_k_scale). Token t of sequence b lands at position
+    pos = ctx_lens[b] - q_len + t, page block_table[b][pos // 128], slot
+    pos % 128; tokens outside [0, max_blocks*128) or on an absent page are
+    skipped. NVFP4: per 16-group of y = x / tensor_scale as in
+    nvfp4_quantize_group; FP8 indexer keys: s = fp32(max|k| / 448) (1 when
+    the max is 0), byte = E4M3(k / s). bf16 caches keep the bits."""
+    prm = w.params
+    B, Tq, G = int(prm["num_seqs"]), int(prm["q_len"]), int(prm["num_kv_heads"])
+    maxb, P = int(prm["max_blocks_per_seq"]), int(prm["num_pages"])
+    nvfp4, fp8 = int(prm["kv_dtype"]) == 1, int(prm["idx_dtype"]) == 1
+    out = dict(k_data=w.k_data.copy(), v_data=w.v_data.copy(), idx_k=w.idx_k.copy(),
+               k_scale=None if w.k_scale is None else w.k_scale.copy(),
+               v_scale=None if w.v_scale is None else w.v_scale.copy(),
+               idx_k_scale=None if w.idx_k_scale is None else w.idx_k_scale.copy())
+    for b in range(B):
+        for t in range(Tq):
+            pos = int(w.ctx_lens[b]) - Tq + t
+            if pos < 0 or pos >= maxb * BLOCK:
+                continue
+            page = int(w.block_table[b, pos // BLOCK])
+            if not _page_ok(page, P):
+                continue
+            slot = pos % BLOCK
+            for g in range(G):
+                if not nvfp4:
+                    out["k_data"][page, g, slot, :] = new_k[b, t, g]
+                    out["v_data"][page, g, :, slot] = new_v[b, t, g]
+                    continue
+                yk = bf16_to_f64(new_k[b, t, g]) / float(w.k_tensor_scale)
+                yv = bf16_to_f64(new_v[b, t, g]) / float(w.v_tensor_scale)
+                for c in range(HEAD_DIM // 16):
+                    sc, codes = nvfp4_quantize_group(yk[16 * c:16 * c + 16])
+                    out["k_scale"][page, g, slot, c] = sc
+                    out["k_data"][page, g, slot, 8 * c:8 * c + 8] = (codes[0::2] | (codes[1::2] << 4)).astype(np.uint8)
+                    sc, codes = nvfp4_quantize_group(yv[16 * c:16 * c + 16])
+                    out["v_scale"][page, g, c, slot] = sc
+                    for i in range(16):
+                        d = 16 * c + i
+                        byte = int(out["v_data"][page, g, d, slot // 2])
+                        if slot % 2 == 0:
+                            byte = (byte & 0xF0) | int(codes[i])
+                        else:
+                            byte = (byte & 0x0F) | (int(codes[i]) << 4)
+                        out["v_data"][page, g, d, slot // 2] = byte
+            if not fp8:
+                out["idx_k"][page, slot, :] = new_idx_k[b, t]
+                continue
+            k = bf16_to_f64(new_idx_k[b, t])
+            amax = np.float32(np.max(np.abs(k)))
+            s = np.float32(amax / np.float32(448.0)) if amax > 0 else np.float32(1.0)
+            out["idx_k"][page, slot, :] = e4m3_encode(k / float(s))
+            out["idx_k_scale"][page, slot] = s
+    return out
 
 
 # ------------------------------------------------------------ whole decode

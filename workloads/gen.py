@@ -35,6 +35,7 @@ IDX_DIM = 64
 
 TAG_Q, TAG_IDXQ, TAG_IDXW, TAG_K, TAG_V, TAG_IDXK = 1, 2, 3, 4, 5, 6
 TAG_OUTLIER, TAG_PLANT, TAG_TABLE, TAG_LENS = 7, 8, 9, 10
+TAG_NEWK, TAG_NEWV, TAG_NEWIDX = 11, 12, 13
 
 
 def _ptr(a):
@@ -206,6 +207,36 @@ def make_workload(name, seed, ctx_lens, q_len, num_q_heads, num_kv_heads, idx_he
                     idx_k_scale=idx_k_scale, block_table=bt, ctx_lens=ctx,
                     k_tensor_scale=float(k_tensor_scale), v_tensor_scale=float(v_tensor_scale),
                     planted=planted, recipe=recipe)
+
+
+def make_new_tokens(w, seed, sigma=1.0, extremes=False):
+    """bf16 bits of the q_len new tokens of every sequence of workload `w`:
+    K and V [B][q_len][num_kv_heads][128] and indexer keys [B][q_len][64],
+    drawn N(0, sigma^2). With `extremes`, token 0 of sequence 0, KV head 0
+    (and its indexer key) gets a saturating group (|x| = 3000), an all-zero
+    group and a group of tiny values (1e-6 scale), so that the quantiser's
+    saturation, zero-scale and subnormal-scale cases occur."""
+    lib = _native.lib()
+    B, Tq, G = w.B, w.Tq, int(w.params["num_kv_heads"])
+    key = lambda tag: lib.msagen_stream_key(int(seed), tag)
+    nk = np.empty((B, Tq, G, HEAD_DIM), dtype=np.uint16)
+    nv = np.empty((B, Tq, G, HEAD_DIM), dtype=np.uint16)
+    ni = np.empty((B, Tq, IDX_DIM), dtype=np.uint16)
+    lib.msagen_normal_bf16(key(TAG_NEWK), 0, nk.size, float(sigma), _ptr(nk))
+    lib.msagen_normal_bf16(key(TAG_NEWV), 0, nv.size, float(sigma), _ptr(nv))
+    lib.msagen_normal_bf16(key(TAG_NEWIDX), 0, ni.size, float(sigma), _ptr(ni))
+    if extremes:
+        def bf16(x):
+            return (np.asarray(x, dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16)
+        sgn = np.where(np.arange(16) % 2 == 0, 1.0, -1.0)
+        for arr in (nk, nv):
+            arr[0, 0, 0, 0:16] = bf16(3000.0 * sgn)
+            arr[0, 0, 0, 16:32] = 0
+            arr[0, 0, 0, 32:48] = bf16(1e-6 * sgn * np.arange(1, 17))
+        ni[0, 0, 0:16] = 0
+        if Tq > 1:
+            ni[0, 1, :] = 0
+    return nk, nv, ni
 
 
 # ----------------------------------------------------------------- configs

@@ -55,13 +55,14 @@ def source_sha(names):
 
 def indexer_bytes(w):
     """Algorithmic bytes of the indexer + pool launch: every visible indexer
-    key (64 B codes + 4 B scale for FP8, 128 B for bf16), indexer queries and
+    key (64 B codes + 4 B scale for FP8, 32 B codes + 4 B scales for NVFP4,
+    128 B for bf16), indexer queries and
     weights, block-table entries read, pooled scores written."""
     prm = w.params
     B, Tq, Hi, maxb = prm["num_seqs"], prm["q_len"], prm["idx_heads"], prm["max_blocks_per_seq"]
     L = np.minimum(w.ctx_lens.astype(np.int64), maxb * 128)
     nblk = (L + 127) // 128
-    per_tok = 68 if prm["idx_dtype"] == 1 else 128
+    per_tok = {0: 128, 1: 68, 2: 36}[int(prm["idx_dtype"])]  # bf16, FP8 (+fp32 scale), NVFP4 (+4 E4M3)
     return int(L.sum() * per_tok + B * Tq * Hi * (64 * 2 + 4) + nblk.sum() * 4 + Tq * nblk.sum() * 4)
 
 
@@ -175,6 +176,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=3)
+    ap.add_argument("--idx-dtype", choices=("fp8", "nvfp4"), default="fp8",
+                    help="indexer-key format (the measured configurations use fp8)")
     ap.add_argument("--replicas", type=int, default=0, help="input copies rotated per step (0: auto)")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -184,8 +187,9 @@ def main():
                     help="write profiles/traffic.json from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE counter "
                          "collections of a --profile-steps run, and exit")
     args = ap.parse_args()
+    wkey = str(args.config) if args.idx_dtype == "fp8" else "%d/%s" % (args.config, args.idx_dtype)
     if args.traffic_from:
-        write_traffic_record(args.traffic_from[0], args.traffic_from[1], args.config)
+        write_traffic_record(args.traffic_from[0], args.traffic_from[1], wkey)
         return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (one GPU's share of the decode "
@@ -195,10 +199,10 @@ def main():
     import torch
     sys.path.insert(0, ROOT)
     import block_sparse_attention_kv_amd as msa
-    from workloads import make_config, CONFIG_NAMES
+    from workloads import make_config, CONFIG_NAMES, IDX_NVFP4
 
     t0 = time.perf_counter()
-    w = make_config(args.config)
+    w = make_config(args.config, idx_dtype=IDX_NVFP4 if args.idx_dtype == "nvfp4" else None)
     log("generated %s in %.1f s (%.2f GB host)" % (w.name, time.perf_counter() - t0, w.nbytes() / 1e9))
     prm = w.params
     B, Tq, Hq = prm["num_seqs"], prm["q_len"], prm["num_q_heads"]
@@ -315,7 +319,7 @@ def main():
     idx_gbps = idx_b / (stage_ms[0] * 1e-3) / 1e9
     att_gbps = att_b / (stage_ms[1] * 1e-3) / 1e9
     step_gbps = step_b / (ms_step * 1e-3) / 1e9
-    rec = traffic_record(args.config)
+    rec = traffic_record(wkey)
     tokens = B * Tq
     res = {
         "metric": METRIC,
@@ -328,9 +332,11 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16/bf16 mfma, f32 accumulate (nvfp4 K/V, fp8 idx keys in)",
+        "dtype": "f16/bf16 mfma, f32 accumulate (nvfp4 K/V, %s idx keys in)" % args.idx_dtype,
         "data": "synthetic",
-        "config": {"workload": CONFIG_NAMES[args.config], "config_id": args.config, "batch": B, "q_len": Tq,
+        "config": {"workload": CONFIG_NAMES[args.config] + ("" if args.idx_dtype == "fp8" else
+                                                             ", NVFP4 idx keys instead of FP8"),
+                   "config_id": wkey, "batch": B, "q_len": Tq,
                    "ctx_len": int(w.ctx_lens.max()), "q_heads": Hq, "kv_heads": prm["num_kv_heads"],
                    "idx_heads": prm["idx_heads"], "top_k": prm["top_k"], "block": 128,
                    "input_replicas": R},

@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libmsa.so")
 
 MSA_OK, MSA_ERR_INVALID_ARG, MSA_ERR_UNSUPPORTED, MSA_ERR_WORKSPACE, MSA_ERR_HIP = range(5)
 KV_BF16, KV_NVFP4 = 0, 1
-IDX_BF16, IDX_FP8 = 0, 1
+IDX_BF16, IDX_FP8, IDX_NVFP4 = 0, 1, 2
 NUM_STAGES = 2
 STAGE_NAMES = ("indexer_pool", "select_sparse_attn")
 
@@ -53,7 +53,7 @@ class Cache(ctypes.Structure):
                 ("v_scale", ctypes.c_void_p), ("k_tensor_scale", ctypes.c_float),
                 ("v_tensor_scale", ctypes.c_float), ("idx_k", ctypes.c_void_p),
                 ("idx_k_scale", ctypes.c_void_p), ("block_table", ctypes.c_void_p),
-                ("ctx_lens", ctypes.c_void_p)]
+                ("ctx_lens", ctypes.c_void_p), ("idx_k_tensor_scale", ctypes.c_float)]
 
 
 _lib = None
@@ -132,11 +132,13 @@ class DeviceCache:
     ctx_lens: torch.Tensor
     k_tensor_scale: float = 1.0
     v_tensor_scale: float = 1.0
+    idx_k_tensor_scale: float = 1.0
 
     def c(self):
         return Cache(_v(self.k_data), _v(self.k_scale), _v(self.v_data), _v(self.v_scale),
                      float(self.k_tensor_scale), float(self.v_tensor_scale), _v(self.idx_k),
-                     _v(self.idx_k_scale), _v(self.block_table), _v(self.ctx_lens))
+                     _v(self.idx_k_scale), _v(self.block_table), _v(self.ctx_lens),
+                     float(self.idx_k_tensor_scale))
 
 
 def _v(t):
@@ -160,7 +162,8 @@ def to_device(host, device="cuda"):
     cache = DeviceCache(_dev(host.k_data, device), _dev(host.k_scale, device), _dev(host.v_data, device),
                         _dev(host.v_scale, device), _dev(host.idx_k, device), _dev(host.idx_k_scale, device),
                         _dev(host.block_table, device), _dev(host.ctx_lens, device),
-                        float(host.k_tensor_scale), float(host.v_tensor_scale))
+                        float(host.k_tensor_scale), float(host.v_tensor_scale),
+                        float(getattr(host, "idx_k_tensor_scale", 1.0)))
     qs = dict(q=_dev(host.q, device), idx_q=_dev(host.idx_q, device), idx_w=_dev(host.idx_w, device))
     return Params.from_dict(host.params), cache, qs
 

@@ -41,6 +41,14 @@
 //     sum_h w_h max(0, ks*d_h) = ks * sum_h w_h med3(d_h, 0, ks >= 0 ? inf : -inf)
 // for either sign of ks. The block max over the 16 keys of a lane group is a
 // 4-step DPP reduction inside one 16-lane row.
+//
+// NVFP4 keys (36 bytes per token) [ainewsbites page, section "Getting
+// started and RL support": an NVFP4 indexer KV dtype]: lane group g loads
+// the 8 code bytes of dims 16g..16g+15 and their E4M3 scale, and decodes
+// them to fp16 exactly (E2M1 x E4M3, as in the attention kernel); the query
+// rows of a sequence are scaled into fp16 range by one power of two 2^-e
+// (exact), and 2^e times the per-tensor scale is applied after the head sum
+// like the FP8 per-token scale (the ReLU commutes with a positive factor).
 #include "fmt.hpp"
 #include "msa_internal.hpp"
 
@@ -55,51 +63,68 @@ namespace {
 #endif
 constexpr int kIdxAux = MSA_IDX_NT ? kAuxNT : 0;
 
+// Key formats (the template parameter KF of the kernel).
+constexpr int kKfBf16 = 0, kKfFp8 = 1, kKfNvfp4 = 2;
+
+// Bytes per token of the key codes.
+constexpr uint32_t key_row_bytes(int kf) { return kf == kKfBf16 ? 128u : kf == kKfFp8 ? 64u : 32u; }
+
 // This lane's share of one tile (16 keys x 64 dims): key 16k + l%16,
 // dims 16*(l/16) .. 16*(l/16) + 15.
-template <bool FP8>
+template <int KF>
 struct KTile;
 template <>
-struct KTile<true> {
+struct KTile<kKfFp8> {
   u32x4 v;   // 16 E4M3 codes
   float s;   // the key's fp32 scale
 };
 template <>
-struct KTile<false> {
+struct KTile<kKfBf16> {
   u32x4 v[2];  // 16 bf16 values
+};
+template <>
+struct KTile<kKfNvfp4> {
+  u32x2 c;     // 16 E2M1 codes
+  uint32_t s;  // the group's E4M3 scale (low byte)
 };
 
 // Lane offset (bytes) of this lane's share of tile 0 inside a page; tile k
 // adds 16*k keys.
-template <bool FP8>
+template <int KF>
 __device__ __forceinline__ uint32_t ktile_lane_off(int lane) {
-  return (uint32_t)((lane & 15) * kIdxDim + 16 * (lane >> 4)) * (FP8 ? 1u : 2u);
+  return (uint32_t)(lane & 15) * key_row_bytes(KF) + (key_row_bytes(KF) / 4) * (uint32_t)(lane >> 4);
 }
 
 // Buffer resources of one page's keys and scales (uniform). An absent page
 // gets an empty range, so its loads return zeros without a memory access.
-template <bool FP8>
+template <int KF>
 struct PageRsrc {
   __amdgpu_buffer_rsrc_t keys, scales;
 };
-template <bool FP8>
-__device__ __forceinline__ PageRsrc<FP8> page_rsrc(const IndexerArgs& a, int page, bool absent) {
-  constexpr uint32_t kPageBytes = kBlock * kIdxDim * (FP8 ? 1 : 2);
+template <int KF>
+__device__ __forceinline__ PageRsrc<KF> page_rsrc(const IndexerArgs& a, int page, bool absent) {
+  constexpr uint32_t kPageBytes = kBlock * key_row_bytes(KF);
+  constexpr uint32_t kScaleBytes = kBlock * 4u;  // fp32 per token, or 4 E4M3 per token
   const int pg = absent ? 0 : page;
-  PageRsrc<FP8> r;
+  PageRsrc<KF> r;
   r.keys = make_rsrc(a.idx_k + (size_t)pg * kPageBytes, absent ? 0u : kPageBytes);
-  if constexpr (FP8) r.scales = make_rsrc(a.idx_k_scale + (size_t)pg * kBlock, absent ? 0u : kBlock * 4u);
+  if constexpr (KF != kKfBf16)
+    r.scales = make_rsrc(static_cast<const uint8_t*>(a.idx_k_scale) + (size_t)pg * kScaleBytes,
+                         absent ? 0u : kScaleBytes);
   return r;
 }
 
-template <bool FP8>
-__device__ __forceinline__ void load_ktile(const PageRsrc<FP8>& r, int k, int lane, uint32_t loff, KTile<FP8>& t) {
-  constexpr uint32_t kTileBytes = 16 * kIdxDim * (FP8 ? 1 : 2);
+template <int KF>
+__device__ __forceinline__ void load_ktile(const PageRsrc<KF>& r, int k, int lane, uint32_t loff, KTile<KF>& t) {
+  constexpr uint32_t kTileBytes = 16 * key_row_bytes(KF);
   // the tile offset goes to the scalar offset: one offset register per lane
   const uint32_t soff = kTileBytes * k, voff = loff;
-  if constexpr (FP8) {
+  if constexpr (KF == kKfFp8) {
     t.v = buf_load16<kIdxAux>(r.keys, voff, soff);
     t.s = buf_load4f<kIdxAux>(r.scales, (uint32_t)(4 * (lane & 15)), (uint32_t)(64 * k));
+  } else if constexpr (KF == kKfNvfp4) {
+    t.c = buf_load8<kIdxAux>(r.keys, voff, soff);
+    t.s = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r.scales, 4 * (lane & 15) + (lane >> 4), 64 * k, kIdxAux);
   } else {
     t.v[0] = buf_load16<kIdxAux>(r.keys, voff, soff);
     t.v[1] = buf_load16<kIdxAux>(r.keys, voff + 16, soff);
@@ -130,27 +155,77 @@ struct Shape {
   static constexpr int RT = HQ * NTT;             // row tiles
 };
 
-// Per-sequence state of a wave: A operands, weights, positions.
-template <bool FP8, int HP, int TQ>
-struct SeqState {
-  typedef Shape<HP, TQ> S;
-  bf16x8 qa[S::RT][2];
-  float wr[S::NTT][HP];   // weight of (token 4*tau + g, head h)
-  int pt[S::NTT];         // position of token 4*tau + g
+// MFMA operand type of the key format: fp16 for NVFP4 keys, else bf16.
+template <int KF>
+struct KeyVec {
+  typedef bf16x8 type;
+};
+template <>
+struct KeyVec<kKfNvfp4> {
+  typedef f16x8 type;
 };
 
-template <bool FP8, int HP, int TQ>
-__device__ __forceinline__ void load_seq(const IndexerArgs& a, int b, int Lc, int lane, SeqState<FP8, HP, TQ>& st) {
+// Per-sequence state of a wave: A operands, weights, positions.
+template <int KF, int HP, int TQ>
+struct SeqState {
+  typedef Shape<HP, TQ> S;
+  typename KeyVec<KF>::type qa[S::RT][2];
+  float wr[S::NTT][HP];   // weight of (token 4*tau + g, head h)
+  int pt[S::NTT];         // position of token 4*tau + g
+  float kq;               // factor undoing the fp16 pre-scale of the queries (NVFP4 keys)
+};
+
+template <int KF, int HP, int TQ>
+__device__ __forceinline__ void load_seq(const IndexerArgs& a, int b, int Lc, int lane, SeqState<KF, HP, TQ>& st) {
   typedef Shape<HP, TQ> S;
   const int g = lane >> 4, rr = lane & 15;
+  u32x4 raw[S::RT][2];
 #pragma unroll
   for (int rho = 0; rho < S::RT; rho++) {
     const int t = 4 * (rho / S::HQ) + (rr >> 2), h = 4 * (rho % S::HQ) + (rr & 3);
     const bool ok = (t < a.Tq) && (h < a.Hi);
-    // FP8 keys: step s uses dims 16g + 8s + e; bf16 keys load dims 16g.. too
+    // step s uses dims 16g + 8s + e for every key format
     const u32x4* q = reinterpret_cast<const u32x4*>(a.idx_q + ((size_t)(b * a.Tq + t) * a.Hi + h) * kIdxDim + 16 * g);
 #pragma unroll
-    for (int s = 0; s < 2; s++) st.qa[rho][s] = __builtin_bit_cast(bf16x8, ok ? q[s] : u32x4{0, 0, 0, 0});
+    for (int s = 0; s < 2; s++) raw[rho][s] = ok ? q[s] : u32x4{0, 0, 0, 0};
+  }
+  st.kq = 1.0f;
+  if constexpr (KF == kKfNvfp4) {
+    // one power of two for the sequence's queries: the largest magnitude
+    // lands in [2^14, 2^15), far inside fp16's range
+    float amax = 0.0f;
+#pragma unroll
+    for (int rho = 0; rho < S::RT; rho++)
+#pragma unroll
+      for (int s = 0; s < 2; s++)
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+          const uint32_t w = raw[rho][s][e];
+          amax = fmaxf(amax, fmaxf(fabsf(bf16_bits_to_f32(w & 0xFFFFu)), fabsf(bf16_bits_to_f32(w >> 16))));
+        }
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) amax = fmaxf(amax, shfl_xor(amax, m));
+    // (clamped so that both factors stay normal floats)
+    const int ex = amax > 0.0f ? min(112, max(-112, (int)((__float_as_uint(amax) >> 23) & 255) - 127 - 14)) : 0;
+    const float down = __uint_as_float((uint32_t)(127 - ex) << 23);
+    st.kq = __uint_as_float((uint32_t)(127 + ex) << 23);
+#pragma unroll
+    for (int rho = 0; rho < S::RT; rho++)
+#pragma unroll
+      for (int s = 0; s < 2; s++) {
+        u32x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+          const uint32_t w = raw[rho][s][e];
+          v[e] = f32x2_to_f16x2(bf16_bits_to_f32(w & 0xFFFFu) * down, bf16_bits_to_f32(w >> 16) * down);
+        }
+        st.qa[rho][s] = __builtin_bit_cast(f16x8, v);
+      }
+  } else {
+#pragma unroll
+    for (int rho = 0; rho < S::RT; rho++)
+#pragma unroll
+      for (int s = 0; s < 2; s++) st.qa[rho][s] = __builtin_bit_cast(bf16x8, raw[rho][s]);
   }
 #pragma unroll
   for (int tau = 0; tau < S::NTT; tau++) {
@@ -165,32 +240,43 @@ __device__ __forceinline__ void load_seq(const IndexerArgs& a, int b, int Lc, in
 // Scores of one block held in the ring T (8 tiles of 16 keys); refills the
 // ring with the next block when PREFETCH. mx[tau]: this lane's max over its
 // keys for token 4*tau + g.
-template <bool FP8, int HP, int TQ, bool PREFETCH, bool SCORES>
-__device__ __forceinline__ void score_block(const IndexerArgs& a, KTile<FP8> (&T)[8], const SeqState<FP8, HP, TQ>& st,
+template <int KF, int HP, int TQ, bool PREFETCH, bool SCORES>
+__device__ __forceinline__ void score_block(const IndexerArgs& a, KTile<KF> (&T)[8], const SeqState<KF, HP, TQ>& st,
                                             int b, int lane, uint32_t loff, int blk, bool absent,
-                                            const PageRsrc<FP8>& rn, float (&mx)[Shape<HP, TQ>::NTT]) {
+                                            const PageRsrc<KF>& rn, float (&mx)[Shape<HP, TQ>::NTT]) {
   typedef Shape<HP, TQ> S;
   const int g = lane >> 4;
 #pragma unroll
   for (int tau = 0; tau < S::NTT; tau++) mx[tau] = -INFINITY;
 #pragma unroll
   for (int k = 0; k < 8; k++) {
-    bf16x8 kb[2];
-    if constexpr (FP8) {
-      kb[0] = __builtin_bit_cast(bf16x8, fp8x8_bf16(T[k].v.x, T[k].v.y));
-      kb[1] = __builtin_bit_cast(bf16x8, fp8x8_bf16(T[k].v.z, T[k].v.w));
-    } else {
-      kb[0] = __builtin_bit_cast(bf16x8, T[k].v[0]);
-      kb[1] = __builtin_bit_cast(bf16x8, T[k].v[1]);
-    }
+    typedef typename KeyVec<KF>::type vec;
+    vec kb[2];
     float ks = 1.0f;
-    if constexpr (FP8) ks = T[k].s;
-    if constexpr (PREFETCH) load_ktile<FP8>(rn, k, lane, loff, T[k]);
+    if constexpr (KF == kKfFp8) {
+      kb[0] = __builtin_bit_cast(vec, fp8x8_bf16(T[k].v.x, T[k].v.y));
+      kb[1] = __builtin_bit_cast(vec, fp8x8_bf16(T[k].v.z, T[k].v.w));
+      ks = T[k].s;
+    } else if constexpr (KF == kKfNvfp4) {
+      const uint32_t s2 = bcast_lo16(fp8x2_f16x2<false>(T[k].s));
+      kb[0] = __builtin_bit_cast(vec, nvfp4x8_f16(T[k].c.x, s2));
+      kb[1] = __builtin_bit_cast(vec, nvfp4x8_f16(T[k].c.y, s2));
+      ks = a.idx_ts * st.kq;
+    } else {
+      kb[0] = __builtin_bit_cast(vec, T[k].v[0]);
+      kb[1] = __builtin_bit_cast(vec, T[k].v[1]);
+    }
+    if constexpr (PREFETCH) load_ktile<KF>(rn, k, lane, loff, T[k]);
     f32x4 acc[S::RT];
 #pragma unroll
     for (int rho = 0; rho < S::RT; rho++) {
-      acc[rho] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(st.qa[rho][0], kb[0], f32x4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
-      acc[rho] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(st.qa[rho][1], kb[1], acc[rho], 0, 0, 0);
+      if constexpr (KF == kKfNvfp4) {
+        acc[rho] = __builtin_amdgcn_mfma_f32_16x16x32_f16(st.qa[rho][0], kb[0], f32x4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+        acc[rho] = __builtin_amdgcn_mfma_f32_16x16x32_f16(st.qa[rho][1], kb[1], acc[rho], 0, 0, 0);
+      } else {
+        acc[rho] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(st.qa[rho][0], kb[0], f32x4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+        acc[rho] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(st.qa[rho][1], kb[1], acc[rho], 0, 0, 0);
+      }
     }
     const float bound = ks >= 0.0f ? INFINITY : -INFINITY;
     const int pos = blk * kBlock + 16 * k + (lane & 15);
@@ -223,20 +309,20 @@ __device__ __forceinline__ int work_blocks(const IndexerArgs& a, int b) {
 
 // Waves per SIMD each instantiation is compiled for (its register budget:
 // 4 -> 128 VGPRs, 3 -> 168, 2 -> 256). bf16 keys need twice the ring.
-constexpr int indexer_occupancy(bool fp8, int hp, int tq) {
-  return !fp8 ? 2 : (hp == 4 && tq > 4) ? 3 : 4;
+constexpr int indexer_occupancy(int kf, int hp, int tq) {
+  return kf == kKfBf16 ? 2 : (hp == 4 && tq > 4) ? 3 : 4;
 }
 
 // SCORES: write every key's score instead of the pooled block maxima.
-template <bool FP8, int HP, int TQ, bool SCORES>
-__global__ __launch_bounds__(256, indexer_occupancy(FP8, HP, TQ)) void indexer_pool_kernel(IndexerArgs a) {
+template <int KF, int HP, int TQ, bool SCORES>
+__global__ __launch_bounds__(256, indexer_occupancy(KF, HP, TQ)) void indexer_pool_kernel(IndexerArgs a) {
   typedef Shape<HP, TQ> S;
   static_assert(S::RT <= 2, "at most 32 query rows");
   extern __shared__ int32_t prefix[];  // [B + 1]: first work block of each sequence
   __shared__ int32_t wsum[4];
   const int tid = threadIdx.x, lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps loop control scalar
-  const uint32_t loff = ktile_lane_off<FP8>(lane);
+  const uint32_t loff = ktile_lane_off<KF>(lane);
 
   // ---- prefix sum of work blocks over the batch (each thread: a run of
   // consecutive sequences)
@@ -290,8 +376,8 @@ __global__ __launch_bounds__(256, indexer_occupancy(FP8, HP, TQ)) void indexer_p
     const int blk_first = (int)(gcur - seq_first);
     const int Lc = clamp_ctx(a.ctx_lens[b], a.maxb);
     const int nblk = (Lc + kBlock - 1) / kBlock;
-    SeqState<FP8, HP, TQ> st;
-    load_seq<FP8, HP, TQ>(a, b, Lc, lane, st);
+    SeqState<KF, HP, TQ> st;
+    load_seq<KF, HP, TQ>(a, b, Lc, lane, st);
 
     for (int w0 = blk_first; w0 < blk_first + (int)(seg_end - gcur); w0 += 64) {
       const int nb = min(64, blk_first + (int)(seg_end - gcur) - w0);
@@ -301,12 +387,12 @@ __global__ __launch_bounds__(256, indexer_occupancy(FP8, HP, TQ)) void indexer_p
         const int pg = a.block_table[(size_t)b * a.maxb + w0 + lane];
         if (pg >= 0 && pg < a.num_pages) mypage = pg;
       }
-      KTile<FP8> T[8];
+      KTile<KF> T[8];
       {
         const int pg = __builtin_amdgcn_readfirstlane(mypage);
-        const PageRsrc<FP8> r0 = page_rsrc<FP8>(a, pg, pg < 0);
+        const PageRsrc<KF> r0 = page_rsrc<KF>(a, pg, pg < 0);
 #pragma unroll
-        for (int k = 0; k < 8; k++) load_ktile<FP8>(r0, k, lane, loff, T[k]);
+        for (int k = 0; k < 8; k++) load_ktile<KF>(r0, k, lane, loff, T[k]);
       }
       // P[tau][g2]: lane i holds the max of block w0 + i for token 4*tau + g2
       float P[S::NTT][4];
@@ -332,13 +418,13 @@ __global__ __launch_bounds__(256, indexer_occupancy(FP8, HP, TQ)) void indexer_p
       for (; i + 1 < nb; i++) {
         const bool absent = __builtin_amdgcn_readlane(mypage, i) < 0;
         const int pgn = __builtin_amdgcn_readlane(mypage, i + 1);
-        const PageRsrc<FP8> rn = page_rsrc<FP8>(a, pgn, pgn < 0);
-        score_block<FP8, HP, TQ, true, SCORES>(a, T, st, b, lane, loff, w0 + i, absent, rn, mx);
+        const PageRsrc<KF> rn = page_rsrc<KF>(a, pgn, pgn < 0);
+        score_block<KF, HP, TQ, true, SCORES>(a, T, st, b, lane, loff, w0 + i, absent, rn, mx);
         keep_max(i);
       }
       {
         const bool absent = __builtin_amdgcn_readlane(mypage, i) < 0;
-        score_block<FP8, HP, TQ, false, SCORES>(a, T, st, b, lane, loff, w0 + i, absent, PageRsrc<FP8>{}, mx);
+        score_block<KF, HP, TQ, false, SCORES>(a, T, st, b, lane, loff, w0 + i, absent, PageRsrc<KF>{}, mx);
         keep_max(i);
       }
       if constexpr (!SCORES) {
@@ -371,15 +457,15 @@ int persistent_grid(const IndexerArgs& a, int occupancy, size_t lds) {
   return (int)(grid < 1 ? 1 : grid);
 }
 
-template <bool FP8, int HP, bool SCORES>
+template <int KF, int HP, bool SCORES>
 hipError_t launch_hp(const IndexerArgs& a, hipStream_t s, const KTimer* tm) {
   const size_t lds = ((size_t)a.B + 1) * sizeof(int32_t);
   switch (a.Tq) {
 #define MSA_TQ_CASE(T)                                                                                 \
   case T:                                                                                              \
     if constexpr (Shape<HP, T>::RT <= 2) {                                                             \
-      const int grid = persistent_grid(a, indexer_occupancy(FP8, HP, T), lds);                         \
-      return launch_kernel(indexer_pool_kernel<FP8, HP, T, SCORES>, dim3(grid), dim3(256), lds, s, a, tm); \
+      const int grid = persistent_grid(a, indexer_occupancy(KF, HP, T), lds);                          \
+      return launch_kernel(indexer_pool_kernel<KF, HP, T, SCORES>, dim3(grid), dim3(256), lds, s, a, tm); \
     }                                                                                                  \
     break;
     MSA_TQ_CASE(1)
@@ -399,15 +485,21 @@ hipError_t launch_hp(const IndexerArgs& a, hipStream_t s, const KTimer* tm) {
 
 }  // namespace
 
-hipError_t launch_indexer(const IndexerArgs& a, bool fp8, int hp, hipStream_t s, const KTimer* tm) {
+template <int KF>
+hipError_t launch_kf(const IndexerArgs& a, int hp, hipStream_t s, const KTimer* tm) {
+  if (a.scores) return hp == 8 ? launch_hp<KF, 8, true>(a, s, tm) : launch_hp<KF, 4, true>(a, s, tm);
+  return hp == 8 ? launch_hp<KF, 8, false>(a, s, tm) : launch_hp<KF, 4, false>(a, s, tm);
+}
+
+hipError_t launch_indexer(const IndexerArgs& a, int key_format, int hp, hipStream_t s, const KTimer* tm) {
   if ((a.scores != nullptr) == (a.pooled != nullptr)) return hipErrorInvalidValue;
   if (a.B < 1 || a.B > kIndexerMaxSeqs || a.cus < 1 || a.wgs_per_cu < 1) return hipErrorInvalidValue;
-  if (a.scores) {
-    if (fp8) return hp == 8 ? launch_hp<true, 8, true>(a, s, tm) : launch_hp<true, 4, true>(a, s, tm);
-    return hp == 8 ? launch_hp<false, 8, true>(a, s, tm) : launch_hp<false, 4, true>(a, s, tm);
+  switch (key_format) {
+    case kKfBf16: return launch_kf<kKfBf16>(a, hp, s, tm);
+    case kKfFp8: return launch_kf<kKfFp8>(a, hp, s, tm);
+    case kKfNvfp4: return launch_kf<kKfNvfp4>(a, hp, s, tm);
+    default: return hipErrorInvalidValue;
   }
-  if (fp8) return hp == 8 ? launch_hp<true, 8, false>(a, s, tm) : launch_hp<true, 4, false>(a, s, tm);
-  return hp == 8 ? launch_hp<false, 8, false>(a, s, tm) : launch_hp<false, 4, false>(a, s, tm);
 }
 
 }  // namespace msa

@@ -12,11 +12,12 @@
 // largest magnitude to E4M3's largest value 448.
 //
 // Work split: one workgroup per (sequence, KV head, chunk of 64 new tokens)
-// for K and V, and one per (sequence, chunk) for the indexer keys. Every
-// group's rounding decisions are taken on IEEE double values, so they are
-// exact for bf16 inputs with a unit tensor scale (a quotient of a bf16 value
-// by an E4M3 value never lies within double rounding of a midpoint unless
-// it is one). In the dim-major V page one byte holds two consecutive tokens;
+// for K and V, and one per (sequence, chunk) for the indexer keys (one wave
+// per token, lane = dim; NVFP4 indexer keys use the K/V quantiser per group
+// of 16 lanes). Every rounding decision is taken on IEEE double values, so
+// it is exact for bf16 inputs with a unit tensor scale (a quotient of a bf16
+// value by an E4M3 value never lies within double rounding of a midpoint
+// unless it is one). In the dim-major V page one byte holds two consecutive tokens;
 // each touched byte has one owning thread (the new token in its even slot,
 // or the first new token when it starts in an odd slot), which merges the
 // new nibbles with the kept one, so workgroups never write the same byte.
@@ -117,18 +118,33 @@ __global__ __launch_bounds__(256) void insert_kernel(InsertArgs a) {
       if (page < 0) continue;  // uniform over the wave
       const uint16_t bits = a.new_idx_k[((size_t)b * a.Tq + t0 + tl) * kIdxDim + lane];
       const size_t row = (size_t)page * kBlock + slot;
-      if (!a.idx_fp8) {
+      if (a.idx_format == 0) {  // bf16
         reinterpret_cast<uint16_t*>(a.idx_k)[row * kIdxDim + lane] = bits;
         continue;
       }
       const float x = bf16_bits_to_f32(bits);
-      float amax = fabsf(x);
+      if (a.idx_format == 1) {  // FP8, one fp32 scale per token
+        float amax = fabsf(x);
 #pragma unroll
-      for (int m = 1; m < 64; m <<= 1) amax = fmaxf(amax, shfl_xor(amax, m));
-      const float s = amax > 0.0f ? __fdiv_rn(amax, 448.0f) : 1.0f;
-      const uint32_t mag = e4m3_mag_code(fabs((double)x / (double)s));
-      a.idx_k[row * kIdxDim + lane] = (uint8_t)(mag | ((x < 0.0f && mag != 0u) ? 0x80u : 0u));
-      if (lane == 0) a.idx_k_scale[row] = s;
+        for (int m = 1; m < 64; m <<= 1) amax = fmaxf(amax, shfl_xor(amax, m));
+        const float s = amax > 0.0f ? __fdiv_rn(amax, 448.0f) : 1.0f;
+        const uint32_t mag = e4m3_mag_code(fabs((double)x / (double)s));
+        a.idx_k[row * kIdxDim + lane] = (uint8_t)(mag | ((x < 0.0f && mag != 0u) ? 0x80u : 0u));
+        if (lane == 0) static_cast<float*>(a.idx_k_scale)[row] = s;
+        continue;
+      }
+      // NVFP4: the 16 lanes of a group share one E4M3 scale
+      const double y = (double)x / a.idx_ts;
+      double amax = fabs(y);
+#pragma unroll
+      for (int m = 1; m < 16; m <<= 1) amax = fmax(amax, shfl_xor(amax, m));
+      const uint32_t scode = e4m3_mag_code(amax / 6.0);
+      const double s = e4m3_mag_value(scode);
+      const uint32_t mag = s > 0.0 ? e2m1_mag_code(fabs(y / s)) : 0u;
+      const uint32_t code = mag | ((y < 0.0 && mag != 0u) ? 8u : 0u);
+      const uint32_t hi = (uint32_t)shfl_xor((int)code, 1);  // the odd dim's code
+      if ((lane & 1) == 0) a.idx_k[row * (kIdxDim / 2) + lane / 2] = (uint8_t)(code | (hi << 4));
+      if ((lane & 15) == 0) static_cast<uint8_t*>(a.idx_k_scale)[row * 4 + lane / 16] = (uint8_t)scode;
     }
     return;
   }

@@ -58,7 +58,7 @@ msa_status_t check_params(const msa_params_t* p) {
     return fail(MSA_ERR_UNSUPPORTED, "too many (sequence, token, head) items");
   if (p->kv_dtype != MSA_KV_BF16 && p->kv_dtype != MSA_KV_NVFP4)
     return fail(MSA_ERR_UNSUPPORTED, "kv_dtype %d", p->kv_dtype);
-  if (p->idx_dtype != MSA_IDX_BF16 && p->idx_dtype != MSA_IDX_FP8_E4M3)
+  if (p->idx_dtype != MSA_IDX_BF16 && p->idx_dtype != MSA_IDX_FP8_E4M3 && p->idx_dtype != MSA_IDX_NVFP4)
     return fail(MSA_ERR_UNSUPPORTED, "idx_dtype %d", p->idx_dtype);
   if (!(p->softmax_scale == p->softmax_scale)) return fail(MSA_ERR_INVALID_ARG, "softmax_scale is NaN");
   return MSA_OK;
@@ -83,6 +83,11 @@ msa_status_t check_cache_idx(const msa_params_t* p, const msa_cache_t* c) {
   if (!c->idx_k) return fail(MSA_ERR_INVALID_ARG, "idx_k is NULL");
   if (p->idx_dtype == MSA_IDX_FP8_E4M3 && !c->idx_k_scale)
     return fail(MSA_ERR_INVALID_ARG, "FP8 indexer keys need idx_k_scale");
+  if (p->idx_dtype == MSA_IDX_NVFP4) {
+    if (!c->idx_k_scale) return fail(MSA_ERR_INVALID_ARG, "NVFP4 indexer keys need idx_k_scale");
+    if (!isfinite(c->idx_k_tensor_scale))
+      return fail(MSA_ERR_INVALID_ARG, "idx_k_tensor_scale must be finite");
+  }
   if (p->idx_dtype == MSA_IDX_BF16 && c->idx_k_scale)
     return fail(MSA_ERR_INVALID_ARG, "bf16 indexer keys take no idx_k_scale");
   if (!c->block_table || !c->ctx_lens) return fail(MSA_ERR_INVALID_ARG, "block_table / ctx_lens is NULL");
@@ -137,6 +142,7 @@ IndexerArgs indexer_args(const msa_params_t* p, const msa_cache_t* c, const void
   a.ctx_lens = c->ctx_lens;
   a.idx_k = static_cast<const uint8_t*>(c->idx_k);
   a.idx_k_scale = c->idx_k_scale;
+  a.idx_ts = c->idx_k_tensor_scale;
   a.idx_q = static_cast<const uint16_t*>(idx_q);
   a.idx_w = idx_w;
   a.pooled = nullptr;
@@ -212,7 +218,7 @@ msa_status_t msa_indexer_scores(const msa_params_t* p, const msa_cache_t* c, con
   if (!idx_q || !idx_w || !scores) return fail(MSA_ERR_INVALID_ARG, "idx_q / idx_w / scores is NULL");
   IndexerArgs a = indexer_args(p, c, idx_q, idx_w);
   a.scores = scores;
-  hipError_t e = launch_indexer(a, p->idx_dtype == MSA_IDX_FP8_E4M3, p->idx_heads <= 4 ? 4 : 8,
+  hipError_t e = launch_indexer(a, p->idx_dtype, p->idx_heads <= 4 ? 4 : 8,
                                 static_cast<hipStream_t>(stream));
   return e == hipSuccess ? MSA_OK : hip_fail(e, "indexer launch");
 }
@@ -274,7 +280,7 @@ msa_status_t msa_decode_layer_traced(const msa_params_t* p, const msa_cache_t* c
   IndexerArgs ia = indexer_args(p, c, idx_q, idx_w);
   ia.pooled = pooled;
   const KTimer t0 = stage_timer(ev, 0), t1 = stage_timer(ev, 1);
-  hipError_t e = launch_indexer(ia, p->idx_dtype == MSA_IDX_FP8_E4M3, p->idx_heads <= 4 ? 4 : 8, s, &t0);
+  hipError_t e = launch_indexer(ia, p->idx_dtype, p->idx_heads <= 4 ? 4 : 8, s, &t0);
   if (e != hipSuccess) return hip_fail(e, "indexer launch");
 
   // selection (from the pooled scores) fused into the attention kernel
@@ -304,7 +310,7 @@ msa_status_t msa_kv_insert(const msa_params_t* p, const msa_cache_t* c, const vo
     return fail(MSA_ERR_UNSUPPORTED, "max_blocks_per_seq %d > %d", p->max_blocks_per_seq, MSA_MAX_BLOCKS);
   if (p->kv_dtype != MSA_KV_BF16 && p->kv_dtype != MSA_KV_NVFP4)
     return fail(MSA_ERR_UNSUPPORTED, "kv_dtype %d", p->kv_dtype);
-  if (p->idx_dtype != MSA_IDX_BF16 && p->idx_dtype != MSA_IDX_FP8_E4M3)
+  if (p->idx_dtype != MSA_IDX_BF16 && p->idx_dtype != MSA_IDX_FP8_E4M3 && p->idx_dtype != MSA_IDX_NVFP4)
     return fail(MSA_ERR_UNSUPPORTED, "idx_dtype %d", p->idx_dtype);
   if ((int64_t)p->q_len > (int64_t)65535 * 64) return fail(MSA_ERR_UNSUPPORTED, "q_len %d too large", p->q_len);
   if ((int64_t)p->num_seqs * (p->num_kv_heads + 1) > 0x7FFFFFFF)
@@ -314,6 +320,8 @@ msa_status_t msa_kv_insert(const msa_params_t* p, const msa_cache_t* c, const vo
   if ((st = check_cache_idx(p, c)) != MSA_OK) return st;
   if (p->kv_dtype == MSA_KV_NVFP4 && (c->k_tensor_scale == 0.0f || c->v_tensor_scale == 0.0f))
     return fail(MSA_ERR_INVALID_ARG, "tensor scales must be nonzero");
+  if (p->idx_dtype == MSA_IDX_NVFP4 && c->idx_k_tensor_scale == 0.0f)
+    return fail(MSA_ERR_INVALID_ARG, "idx_k_tensor_scale must be nonzero");
   if (!new_k || !new_v || !new_idx_k) return fail(MSA_ERR_INVALID_ARG, "new_k / new_v / new_idx_k is NULL");
   InsertArgs a;
   a.block_table = c->block_table;
@@ -323,19 +331,20 @@ msa_status_t msa_kv_insert(const msa_params_t* p, const msa_cache_t* c, const vo
   a.v_data = static_cast<uint8_t*>(const_cast<void*>(c->v_data));
   a.v_scale = static_cast<uint8_t*>(const_cast<void*>(c->v_scale));
   a.idx_k = static_cast<uint8_t*>(const_cast<void*>(c->idx_k));
-  a.idx_k_scale = const_cast<float*>(c->idx_k_scale);
+  a.idx_k_scale = const_cast<void*>(c->idx_k_scale);
   a.new_k = static_cast<const uint16_t*>(new_k);
   a.new_v = static_cast<const uint16_t*>(new_v);
   a.new_idx_k = static_cast<const uint16_t*>(new_idx_k);
   a.k_ts = (double)c->k_tensor_scale;
   a.v_ts = (double)c->v_tensor_scale;
+  a.idx_ts = (double)c->idx_k_tensor_scale;
   a.B = p->num_seqs;
   a.Tq = p->q_len;
   a.Hkv = p->num_kv_heads;
   a.maxb = p->max_blocks_per_seq;
   a.num_pages = p->num_pages;
   a.nvfp4 = p->kv_dtype == MSA_KV_NVFP4;
-  a.idx_fp8 = p->idx_dtype == MSA_IDX_FP8_E4M3;
+  a.idx_format = p->idx_dtype;
   hipError_t e = launch_insert(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? MSA_OK : hip_fail(e, "insert launch");
 }

@@ -11,8 +11,9 @@ namespace msa {
 struct IndexerArgs {
   const int32_t* block_table;  // [B][maxb]
   const int32_t* ctx_lens;     // [B]
-  const uint8_t* idx_k;        // FP8 u8[P][128][64] or bf16 [P][128][64]
-  const float* idx_k_scale;    // [P][128] (FP8 only)
+  const uint8_t* idx_k;        // FP8 u8[P][128][64], NVFP4 u8[P][128][32] or bf16 [P][128][64]
+  const void* idx_k_scale;     // FP8 f32[P][128], NVFP4 u8[P][128][4], bf16 none
+  float idx_ts;                // NVFP4 per-tensor scale
   const uint16_t* idx_q;       // bf16 [B][Tq][Hi][64]
   const float* idx_w;          // [B][Tq][Hi]
   float* pooled;               // [B][Tq][maxb] or nullptr
@@ -71,14 +72,14 @@ struct InsertArgs {
   uint8_t* k_scale;            // u8[P][G][128][8] (NVFP4)
   uint8_t* v_data;             // NVFP4 u8[P][G][128 d][64] or bf16 [P][G][128 d][128]
   uint8_t* v_scale;            // u8[P][G][8][128] (NVFP4)
-  uint8_t* idx_k;              // FP8 u8[P][128][64] or bf16 [P][128][64]
-  float* idx_k_scale;          // [P][128] (FP8)
+  uint8_t* idx_k;              // FP8 u8[P][128][64], NVFP4 u8[P][128][32] or bf16 [P][128][64]
+  void* idx_k_scale;           // FP8 f32[P][128], NVFP4 u8[P][128][4]
   const uint16_t* new_k;       // bf16 [B][Tq][G][128]
   const uint16_t* new_v;       // bf16 [B][Tq][G][128]
   const uint16_t* new_idx_k;   // bf16 [B][Tq][64]
-  double k_ts, v_ts;           // tensor scales (NVFP4)
+  double k_ts, v_ts, idx_ts;   // tensor scales (NVFP4)
   int B, Tq, Hkv, maxb, num_pages;
-  int nvfp4, idx_fp8;
+  int nvfp4, idx_format;       // idx_format: msa_idx_dtype_t
 };
 
 // Kernel timing hook: when either event is set, the kernel is dispatched with
@@ -103,7 +104,8 @@ hipError_t launch_kernel(void (*kern)(Args), dim3 grid, dim3 block, size_t lds, 
   return hipGetLastError();
 }
 
-hipError_t launch_indexer(const IndexerArgs& a, bool fp8, int hp, hipStream_t s, const KTimer* t = nullptr);
+// key_format: msa_idx_dtype_t (0 bf16, 1 FP8, 2 NVFP4)
+hipError_t launch_indexer(const IndexerArgs& a, int key_format, int hp, hipStream_t s, const KTimer* t = nullptr);
 hipError_t launch_select(const SelectArgs& a, hipStream_t s);
 hipError_t launch_insert(const InsertArgs& a, hipStream_t s);
 hipError_t launch_attn(const AttnArgs& a, bool nvfp4, int waves, hipStream_t s, const KTimer* t = nullptr);

@@ -80,6 +80,12 @@
  * idx_dtype == MSA_IDX_FP8_E4M3:
  *   idx_k       u8[P][128 tok][64]  OCP E4M3 codes
  *   idx_k_scale f32[P][128 tok]     key = e4m3(code) * idx_k_scale[tok]
+ * idx_dtype == MSA_IDX_NVFP4 (36 bytes per token instead of 68) [ainewsbites
+ *   page, section "Getting started and RL support": the NVIDIA setup runs
+ *   the indexer keys in NVFP4 too]:
+ *   idx_k       u8[P][128 tok][32]  E2M1 codes, dim 2i in the low nibble
+ *   idx_k_scale u8[P][128 tok][4]   E4M3 scale of dims [16c, 16c+16)
+ *   key = e2m1 * e4m3 * idx_k_tensor_scale
  * idx_dtype == MSA_IDX_BF16:
  *   idx_k       bf16[P][128 tok][64], idx_k_scale must be NULL.
  *
@@ -114,7 +120,7 @@ typedef enum {
 } msa_status_t;
 
 typedef enum { MSA_KV_BF16 = 0, MSA_KV_NVFP4 = 1 } msa_kv_dtype_t;
-typedef enum { MSA_IDX_BF16 = 0, MSA_IDX_FP8_E4M3 = 1 } msa_idx_dtype_t;
+typedef enum { MSA_IDX_BF16 = 0, MSA_IDX_FP8_E4M3 = 1, MSA_IDX_NVFP4 = 2 } msa_idx_dtype_t;
 
 /* Problem description (host struct). Supported: head_dim 128, idx_dim 64,
  * block_size 128, 1 <= top_k <= 16, keep_last in {0,1},
@@ -149,9 +155,10 @@ typedef struct {
   float k_tensor_scale;       /* per-tensor fp32 scale of K (NVFP4 only) */
   float v_tensor_scale;       /* per-tensor fp32 scale of V (NVFP4 only) */
   const void* idx_k;
-  const float* idx_k_scale;   /* NULL for MSA_IDX_BF16 */
+  const void* idx_k_scale;    /* FP8: f32[P][128]; NVFP4: u8[P][128][4]; NULL for MSA_IDX_BF16 */
   const int32_t* block_table; /* device i32[B][max_blocks_per_seq] */
   const int32_t* ctx_lens;    /* device i32[B] */
+  float idx_k_tensor_scale;   /* per-tensor fp32 scale of NVFP4 indexer keys (ignored otherwise) */
 } msa_cache_t;
 
 /* Bytes of workspace msa_decode_layer and msa_sparse_attn_decode need for
@@ -246,6 +253,8 @@ msa_status_t msa_decode_layer_traced(const msa_params_t* p, const msa_cache_t* c
  * that rounds to zero is stored as +0.
  * FP8 indexer keys, per token: s = max|k| / 448 rounded to fp32 (1.0 when
  * the max is 0); byte = E4M3(k / s) (double quotient), idx_k_scale = s.
+ * NVFP4 indexer keys: as NVFP4 K with y = k / idx_k_tensor_scale, per
+ * 16-dim group.
  * bf16 caches store the values unchanged.
  * The cache buffers are written through the pointers of msa_cache_t (their
  * const qualifies the decode calls only). Tokens with pos < 0 or pos >=

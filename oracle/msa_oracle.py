@@ -16,6 +16,7 @@ only, the most recent block is always kept, so at most 2,048 keys per query]:
 
  1. decode   NVFP4 K/V  x = e2m1(code) * e4m3(scale of its 16-group) * ts
              FP8 indexer keys  k = e4m3(code) * per-token fp32 scale
+             NVFP4 indexer keys  k = e2m1(code) * e4m3(16-group scale) * ts
              bf16 values exactly.
  2. position p_t = L_b - T_q + t; keys 0..p_t are visible.
  3. indexer  s_j = sum_h w_h * max(0, <qi_h, k_j>)           (reading c1)
@@ -118,14 +119,18 @@ def seq_indexer_keys(w, b, n_tok):
     nblk = (n_tok + BLOCK - 1) // BLOCK
     keys = np.zeros((nblk * BLOCK, IDX_DIM))
     present = np.zeros(nblk * BLOCK, dtype=bool)
-    fp8 = int(w.params["idx_dtype"]) == 1
+    fmt = int(w.params["idx_dtype"])
     for i in range(min(nblk, maxb)):
         page = int(w.block_table[b, i])
         if not _page_ok(page, P):
             continue
         sl = slice(i * BLOCK, (i + 1) * BLOCK)
-        if fp8:
+        if fmt == 1:
             keys[sl] = e4m3_to_f64(w.idx_k[page]) * w.idx_k_scale[page].astype(np.float64)[:, None]
+        elif fmt == 2:
+            vals = e2m1_to_f64(nibbles(w.idx_k[page]))                       # [tok][64]
+            keys[sl] = vals * np.repeat(e4m3_to_f64(w.idx_k_scale[page]), 16, axis=1) * \
+                float(getattr(w, "idx_k_tensor_scale", 1.0))
         else:
             keys[sl] = bf16_to_f64(w.idx_k[page])
         present[sl] = True
@@ -328,11 +333,12 @@ def kv_insert(w, new_k, new_v, new_idx_k):
     pos % 128; tokens outside [0, max_blocks*128) or on an absent page are
     skipped. NVFP4: per 16-group of y = x / tensor_scale as in
     nvfp4_quantize_group; FP8 indexer keys: s = fp32(max|k| / 448) (1 when
-    the max is 0), byte = E4M3(k / s). bf16 caches keep the bits."""
+    the max is 0), byte = E4M3(k / s); NVFP4 indexer keys as NVFP4 K with
+    the indexer's tensor scale. bf16 caches keep the bits."""
     prm = w.params
     B, Tq, G = int(prm["num_seqs"]), int(prm["q_len"]), int(prm["num_kv_heads"])
     maxb, P = int(prm["max_blocks_per_seq"]), int(prm["num_pages"])
-    nvfp4, fp8 = int(prm["kv_dtype"]) == 1, int(prm["idx_dtype"]) == 1
+    nvfp4, idx_fmt = int(prm["kv_dtype"]) == 1, int(prm["idx_dtype"])
     out = dict(k_data=w.k_data.copy(), v_data=w.v_data.copy(), idx_k=w.idx_k.copy(),
                k_scale=None if w.k_scale is None else w.k_scale.copy(),
                v_scale=None if w.v_scale is None else w.v_scale.copy(),
@@ -367,10 +373,17 @@ def kv_insert(w, new_k, new_v, new_idx_k):
                         else:
                             byte = (byte & 0x0F) | (int(codes[i]) << 4)
                         out["v_data"][page, g, d, slot // 2] = byte
-            if not fp8:
+            if idx_fmt == 0:
                 out["idx_k"][page, slot, :] = new_idx_k[b, t]
                 continue
             k = bf16_to_f64(new_idx_k[b, t])
+            if idx_fmt == 2:
+                y = k / float(getattr(w, "idx_k_tensor_scale", 1.0))
+                for c in range(IDX_DIM // 16):
+                    sc, codes = nvfp4_quantize_group(y[16 * c:16 * c + 16])
+                    out["idx_k_scale"][page, slot, c] = sc
+                    out["idx_k"][page, slot, 8 * c:8 * c + 8] = (codes[0::2] | (codes[1::2] << 4)).astype(np.uint8)
+                continue
             amax = np.float32(np.max(np.abs(k)))
             s = np.float32(amax / np.float32(448.0)) if amax > 0 else np.float32(1.0)
             out["idx_k"][page, slot, :] = e4m3_encode(k / float(s))

@@ -163,6 +163,31 @@ def check_lse(gpu, ref, label=""):
         assert err <= LSE_ABS, (label, "lse", err)
 
 
+def indexer_parity(w, run=None):
+    """Unfused indexer scores, pool and selection vs the oracle for every
+    (sequence, token); returns the number of tie-band selection
+    differences."""
+    run = run or Run(w)
+    sc = run.scores()
+    pooled, sel, nsel = run.pool_select(sc)
+    scn = sc.cpu().numpy().astype(np.float64)
+    ref = O.decode_layer(w, want_scores=True)
+    prm = w.params
+    ties = 0
+    for b in range(prm["num_seqs"]):
+        for t in range(prm["q_len"]):
+            lab = "%s b=%d t=%d" % (w.name, b, t)
+            check_scores(scn[b, t], ref["scores"][b, t], lab)
+            n = int(ref["nsel"][b, t])
+            assert nsel[b, t] == n, lab
+            check_scores(pooled[b, t], ref["pooled"][b, t], lab + " pooled")
+            p_t = min(int(w.ctx_lens[b]), prm["max_blocks_per_seq"] * 128) - prm["q_len"] + t
+            nb = p_t // 128 + 1 if p_t >= 0 else 0
+            ties += check_selection(sel[b, t], ref["pooled"][b, t][:nb], ref["sel"][b, t][:n],
+                                    prm["top_k"], prm["keep_last"], lab)
+    return ties
+
+
 def layer_parity(w, run=None, seqs=None, tokens=None, strict=False):
     """Fused layer vs the oracle for the listed sequences (default all).
     Returns (number of tie-band selection differences, max-abs where

@@ -117,6 +117,29 @@ def test_dtype_scale_consistency_rejected():
         _lib.MSA_ERR_INVALID_ARG       # FP8 keys without idx_k_scale
 
 
+def test_nvfp4_index_keys_and_insert_args_rejected():
+    L = msa.load()
+    fake = ctypes.c_void_p(0x1000)
+    p = _params(kv_dtype=1, idx_dtype=2)
+    c = msa.Cache(fake, fake, fake, fake, 1.0, 1.0, fake, None, fake, fake, 1.0)
+    assert L.msa_indexer_scores(ctypes.byref(p), ctypes.byref(c), fake, fake, fake, None) == \
+        _lib.MSA_ERR_INVALID_ARG       # NVFP4 keys without their scales
+    c = msa.Cache(fake, fake, fake, fake, 1.0, 1.0, fake, fake, fake, fake, float("nan"))
+    assert L.msa_indexer_scores(ctypes.byref(p), ctypes.byref(c), fake, fake, fake, None) == \
+        _lib.MSA_ERR_INVALID_ARG       # non-finite tensor scale
+    p = _params(kv_dtype=1, idx_dtype=3)
+    assert L.msa_indexer_scores(ctypes.byref(p), ctypes.byref(c), fake, fake, fake, None) == \
+        _lib.MSA_ERR_UNSUPPORTED
+    p = _params(kv_dtype=1, idx_dtype=2)
+    c = msa.Cache(fake, fake, fake, fake, 1.0, 1.0, fake, fake, fake, fake, 0.0)
+    assert L.msa_kv_insert(ctypes.byref(p), ctypes.byref(c), fake, fake, fake, None) == \
+        _lib.MSA_ERR_INVALID_ARG       # a zero tensor scale cannot be divided by
+    c = msa.Cache(fake, fake, fake, fake, 1.0, 1.0, fake, fake, fake, fake, 1.0)
+    assert L.msa_kv_insert(ctypes.byref(p), ctypes.byref(c), None, fake, fake, None) == \
+        _lib.MSA_ERR_INVALID_ARG
+    assert L.msa_kv_insert(None, ctypes.byref(c), fake, fake, fake, None) == _lib.MSA_ERR_INVALID_ARG
+
+
 def test_workspace_too_small_rejected():
     L = msa.load()
     fake = ctypes.c_void_p(0x1000)

@@ -42,24 +42,7 @@ def test_dequant_fp8_bitexact():
 @pytest.mark.parametrize("idx", range(4))
 def test_indexer_scores_and_select(idx):
     w = small_cases()[idx]
-    run = G.Run(w)
-    sc = run.scores()
-    pooled, sel, nsel = run.pool_select(sc)
-    scn = sc.cpu().numpy().astype(np.float64)
-    ref = O.decode_layer(w, want_scores=True)
-    prm = w.params
-    ties = 0
-    for b in range(prm["num_seqs"]):
-        for t in range(prm["q_len"]):
-            lab = "%s b=%d t=%d" % (w.name, b, t)
-            G.check_scores(scn[b, t], ref["scores"][b, t], lab)
-            n = int(ref["nsel"][b, t])
-            assert nsel[b, t] == n, lab
-            G.check_scores(pooled[b, t], ref["pooled"][b, t], lab + " pooled")
-            p_t = min(int(w.ctx_lens[b]), prm["max_blocks_per_seq"] * 128) - prm["q_len"] + t
-            nb = p_t // 128 + 1 if p_t >= 0 else 0
-            ties += G.check_selection(sel[b, t], ref["pooled"][b, t][:nb], ref["sel"][b, t][:n],
-                                      prm["top_k"], prm["keep_last"], lab)
+    ties = G.indexer_parity(w)
     print("%s: tie-band selection differences: %d" % (w.name, ties))
 
 

@@ -205,3 +205,59 @@ def test_kv_insert_bf16_cache_keeps_bits():
         assert np.array_equal(out["k_data"][page, 0, slot], nk[b, t, 0])
         assert np.array_equal(out["v_data"][page, 1, :, slot], nv[b, t, 1])
         assert np.array_equal(out["idx_k"][page, slot], ni[b, t])
+
+
+# ------------------------------------------------ NVFP4 indexer keys
+
+def test_nvfp4_index_keys_decode_worked_page():
+    # a page whose slot 3 holds hand-made codes: dims 0/1 = 0.5/1.0 and dims
+    # 30/31 = -6/3 under group scales 1.0 (0x38) and 2.0 (0x40), tensor 0.5
+    from workloads import IDX_NVFP4
+    w = make_workload("nvidx", 71, [256], 1, 8, 1, 4, KV_NVFP4, IDX_NVFP4, table="identity")
+    w.idx_k[0, 3, :] = 0
+    w.idx_k[0, 3, 0] = 0x21            # dim 0 code 1 (0.5), dim 1 code 2 (1.0)
+    w.idx_k[0, 3, 15] = (0x5 << 4) | 0xF  # dim 30 code 15 (-6), dim 31 code 5 (3)
+    w.idx_k_scale[0, 3, :] = [0x38, 0x40, 0x38, 0x38]
+    w.idx_k_tensor_scale = 0.5
+    keys, present = O.seq_indexer_keys(w, 0, 256)
+    want = np.zeros(64)
+    want[0], want[1] = 0.5 * 0.5, 1.0 * 0.5
+    want[30], want[31] = -6 * 2.0 * 0.5, 3 * 2.0 * 0.5
+    assert present[3] and np.array_equal(keys[3], want)
+
+
+def test_nvfp4_index_keys_agree_with_fp8_keys_of_the_same_draws():
+    # the generator quantises the same draws to FP8 (3 mantissa bits, one
+    # scale per token) or to NVFP4 (one E4M3 scale per 16 dims): both decode
+    # to within their own step of the draw, hence of each other
+    from workloads import IDX_NVFP4
+    wf = make_workload("f8", 72, [700, 300], 1, 8, 1, 4, KV_NVFP4, IDX_FP8, table="permute")
+    wn = make_workload("f4", 72, [700, 300], 1, 8, 1, 4, KV_NVFP4, IDX_NVFP4, table="permute")
+    for b in range(2):
+        n = int(wf.ctx_lens[b])
+        kf, _ = O.seq_indexer_keys(wf, b, n)
+        kn, _ = O.seq_indexer_keys(wn, b, n)
+        for c in range(4):
+            gf, gn = kf[:, 16 * c:16 * c + 16], kn[:, 16 * c:16 * c + 16]
+            amax = np.max(np.abs(gf), axis=1, keepdims=True)
+            # NVFP4 step: one scale unit (amax/6 up to 1/16 rounding, or
+            # 2^-10 below the smallest normal E4M3); FP8: 1/16 relative
+            bound = np.maximum(amax / 6 * (1 + 1 / 16), 2.0 ** -10) + np.abs(gf) / 16 + 1e-12
+            assert np.all(np.abs(gf - gn) <= bound)
+
+
+def test_kv_insert_nvfp4_index_keys_brute_force():
+    from workloads import IDX_NVFP4
+    w = make_workload("nvins", 73, [300, 129, 5], 4, 8, 2, 4, KV_NVFP4, IDX_NVFP4, table="permute")
+    w.idx_k_tensor_scale = 0.75
+    nk, nv, ni = make_new_tokens(w, 74, extremes=True)
+    out = O.kv_insert(w, nk, nv, ni)
+    for b, t, page, slot in _written(w):
+        y = O.bf16_to_f64(ni[b, t]) / 0.75
+        codes = O.nibbles(out["idx_k"][page, slot][None])[0]
+        for c in range(4):
+            grp = y[16 * c:16 * c + 16]
+            sc = int(out["idx_k_scale"][page, slot, c])
+            assert sc == _brute_e4m3(np.max(np.abs(grp)) / 6.0)
+            s = float(O.e4m3_to_f64(np.uint8(sc)))
+            assert list(codes[16 * c:16 * c + 16]) == [(_brute_e2m1(v / s) if s > 0 else 0) for v in grp]

@@ -213,13 +213,16 @@ void msagen_kv_cache(uint64_t key_k, uint64_t key_v, int32_t nseq, const int32_t
 /*
  * Indexer keys. For every sequence b and token tok < ctx_lens[b]:
  *   k[d] = sigma * N(key, ...) + (plant[b*max_blocks + tok/128] ? shift[b*64 + d] : 0)
- * FP8 (fp8 != 0): per-token scale s = amax / 448 (fp32; 1.0 when amax == 0),
+ * fmt 1 (FP8): per-token scale s = amax / 448 (fp32; 1.0 when amax == 0),
  * code = E4M3_RNE(k / s) saturating; written idx_k[page][slot][64] and
- * idx_scale[page][slot]. BF16 (fp8 == 0): idx_k holds bf16 codes.
+ * (float) idx_scale[page][slot]. fmt 2 (NVFP4): per 16-dim group scale
+ * E4M3_RNE(amax / 6) and codes E2M1_RNE(k / scale) as for K; written
+ * idx_k[page][slot][32] (dim 2i in the low nibble) and (u8)
+ * idx_scale[page][slot][4]. fmt 0 (BF16): idx_k holds bf16 codes.
  */
 void msagen_idx_cache(uint64_t key, int32_t nseq, const int32_t* ctx_lens, const int32_t* block_table,
                       int32_t max_blocks, double sigma, const uint8_t* plant, const float* shift,
-                      int32_t fp8, void* idx_k, float* idx_scale) {
+                      int32_t fmt, void* idx_k, void* idx_scale) {
   int64_t total = 0;
   for (int32_t b = 0; b < nseq; b++) total += (ctx_lens[b] + 127) / 128;
 #pragma omp parallel for schedule(dynamic, 8)
@@ -244,11 +247,26 @@ void msagen_idx_cache(uint64_t key, int32_t nseq, const int32_t* ctx_lens, const
         x[d] = (float)v;
         amax = fmaxf(amax, fabsf(x[d]));
       }
-      if (fp8) {
+      if (fmt == 1) {
         float s = amax > 0.0f ? amax / 448.0f : 1.0f;
         uint8_t* row = (uint8_t*)idx_k + (page * 128 + slot) * 64;
         for (int d = 0; d < 64; d++) row[d] = e4m3_rne((double)x[d] / (double)s);
-        idx_scale[page * 128 + slot] = s;
+        ((float*)idx_scale)[page * 128 + slot] = s;
+      } else if (fmt == 2) {
+        uint8_t* row = (uint8_t*)idx_k + (page * 128 + slot) * 32;
+        uint8_t* sc = (uint8_t*)idx_scale + (page * 128 + slot) * 4;
+        for (int c = 0; c < 4; c++) {
+          double gmax = 0.0;
+          for (int i = 0; i < 16; i++) gmax = fmax(gmax, fabs((double)x[16 * c + i]));
+          uint8_t scode = e4m3_rne(gmax / 6.0);
+          double sv = e4m3_val_enc(scode);
+          sc[c] = scode;
+          for (int i = 0; i < 16; i += 2) {
+            uint8_t lo = sv > 0.0 ? e2m1_rne((double)x[16 * c + i] / sv) : 0;
+            uint8_t hi = sv > 0.0 ? e2m1_rne((double)x[16 * c + i + 1] / sv) : 0;
+            row[(16 * c + i) / 2] = (uint8_t)(lo | (hi << 4));
+          }
+        }
       } else {
         uint16_t* row = (uint16_t*)idx_k + (page * 128 + slot) * 64;
         for (int d = 0; d < 64; d++) row[d] = bf16_rne(x[d]);

@@ -28,7 +28,7 @@ import numpy as np
 from . import _native
 
 KV_BF16, KV_NVFP4 = 0, 1
-IDX_BF16, IDX_FP8 = 0, 1
+IDX_BF16, IDX_FP8, IDX_NVFP4 = 0, 1, 2
 BLOCK = 128
 HEAD_DIM = 128
 IDX_DIM = 64
@@ -55,11 +55,12 @@ class Workload:
     v_data: np.ndarray       # uint8 [P][G][128][64] (dim-major) or uint16 [P][G][128][128]
     v_scale: Optional[np.ndarray]
     idx_k: np.ndarray        # uint8 [P][128][64] or uint16 [P][128][64]
-    idx_k_scale: Optional[np.ndarray]  # float32 [P][128]
+    idx_k_scale: Optional[np.ndarray]  # FP8 float32 [P][128], NVFP4 uint8 [P][128][4]
     block_table: np.ndarray  # int32 [B][max_blocks]
     ctx_lens: np.ndarray     # int32 [B]
     k_tensor_scale: float = 1.0
     v_tensor_scale: float = 1.0
+    idx_k_tensor_scale: float = 1.0
     planted: Dict[int, List[int]] = field(default_factory=dict)
     recipe: str = ""
 
@@ -190,12 +191,14 @@ def make_workload(name, seed, ctx_lens, q_len, num_q_heads, num_kv_heads, idx_he
     if idx_dtype == IDX_FP8:
         idx_k = np.zeros((num_pages, BLOCK, IDX_DIM), dtype=np.uint8)
         idx_k_scale = np.zeros((num_pages, BLOCK), dtype=np.float32)
+    elif idx_dtype == IDX_NVFP4:
+        idx_k = np.zeros((num_pages, BLOCK, IDX_DIM // 2), dtype=np.uint8)
+        idx_k_scale = np.zeros((num_pages, BLOCK, IDX_DIM // 16), dtype=np.uint8)
     else:
         idx_k = np.zeros((num_pages, BLOCK, IDX_DIM), dtype=np.uint16)
         idx_k_scale = None
     lib.msagen_idx_cache(key(TAG_IDXK), B, _ptr(ctx), _ptr(bt), max_blocks, float(idx_sigma),
-                         _ptr(plant), _ptr(shift), 1 if idx_dtype == IDX_FP8 else 0,
-                         _ptr(idx_k), _ptr(idx_k_scale))
+                         _ptr(plant), _ptr(shift), int(idx_dtype), _ptr(idx_k), _ptr(idx_k_scale))
 
     params = dict(num_seqs=B, q_len=Tq, num_q_heads=Hq, num_kv_heads=G, head_dim=HEAD_DIM,
                   idx_heads=Hi, idx_dim=IDX_DIM, block_size=BLOCK, top_k=int(top_k),
@@ -256,35 +259,37 @@ def ragged_lengths(seed, n, lo=1024, hi=262144):
     return np.floor(np.exp(r.uniform(math.log(lo), math.log(hi), size=n))).astype(np.int32)
 
 
-def make_config(n, seed=None):
-    """One of the five decode configurations (seed defaults to 1000 + n)."""
+def make_config(n, seed=None, idx_dtype=None):
+    """One of the five decode configurations (seed defaults to 1000 + n).
+    idx_dtype overrides the indexer-key format of configurations 2-5 (FP8)."""
     if seed is None:
         seed = 1000 + n
+    idx = IDX_FP8 if idx_dtype is None else int(idx_dtype)
     if n == 1:
         return make_workload("cfg1", seed, [4096], 1, 8, 1, 4, KV_BF16, IDX_BF16,
                              table="identity", n_planted=3,
                              recipe="q,k,v,qi,ki ~ N(0,1) bf16; w ~ U(0,1); identity table; "
                                     "3 planted non-last blocks")
     if n == 2:
-        return make_workload("cfg2", seed, [32768] * 8, 1, 32, 2, 4, KV_NVFP4, IDX_FP8,
+        return make_workload("cfg2", seed, [32768] * 8, 1, 32, 2, 4, KV_NVFP4, idx,
                              table="permute", n_planted=8,
                              recipe="K/V ~ N(0,1) -> NVFP4 (scale E4M3(amax/6), ts 1.0); "
                                     "ki ~ N(0,1) -> FP8 + per-token amax/448; permuted pages; "
                                     "8 planted blocks per sequence")
     if n == 3:
-        return make_workload("cfg3", seed, [131072] * 32, 4, 64, 4, 8, KV_NVFP4, IDX_FP8,
+        return make_workload("cfg3", seed, [131072] * 32, 4, 64, 4, 8, KV_NVFP4, idx,
                              table="permute", outlier_frac=0.01, outlier_mul=8.0,
                              recipe="K/V ~ N(0,1), 2 channels per KV head x8 (K and V), NVFP4; "
                                     "ki ~ N(0,1) FP8; permuted pages; no planting; "
                                     "4 causal query tokens")
     if n == 4:
-        return make_workload("cfg4", seed, [524288] * 4, 1, 64, 4, 4, KV_NVFP4, IDX_FP8,
+        return make_workload("cfg4", seed, [524288] * 4, 1, 64, 4, 4, KV_NVFP4, idx,
                              table="permute", n_planted=16, idx_sigma=0.01,
                              recipe="K/V ~ N(0,1) NVFP4; ki ~ N(0, 0.01^2) FP8 (near-tied "
                                     "pooled scores); 16 planted blocks; permuted pages")
     if n == 5:
         lens = ragged_lengths(seed, 64)
-        return make_workload("cfg5", seed, lens, 1, 48, 4, 8, KV_NVFP4, IDX_FP8,
+        return make_workload("cfg5", seed, lens, 1, 48, 4, 8, KV_NVFP4, idx,
                              max_blocks=2048, table="pool", pool_factor=1.25,
                              recipe="L ~ floor(exp(U(ln 1024, ln 262144))); K/V ~ N(0,1) "
                                     "NVFP4; ki ~ N(0,1) FP8; shared pool of 1.25x pages, "

@@ -25,3 +25,13 @@ def test_config5_ragged_sampled():
     ties, mx, mean = G.layer_parity(w, seqs=seqs, strict=True)
     print("cfg5 sampled %s (lens %s): tie-band selections %d, out max-abs %.2e mean-abs %.2e" % (
         seqs, [int(w.ctx_lens[s]) for s in seqs], ties, mx, mean))
+
+
+@pytest.mark.parametrize("cfg,seqs", [(3, [5]), (4, [1])])
+def test_config_full_size_nvfp4_index_keys_sampled(cfg, seqs):
+    # the same workloads with NVFP4 indexer keys (bench.py --idx-dtype nvfp4)
+    from workloads import IDX_NVFP4
+    w = make_config(cfg, idx_dtype=IDX_NVFP4)
+    ties, mx, mean = G.layer_parity(w, seqs=seqs, strict=True)
+    print("cfg%d nvfp4 keys sampled %s: tie-band selections %d, out max-abs %.2e mean-abs %.2e" % (
+        cfg, seqs, ties, mx, mean))

@@ -95,6 +95,14 @@ def test_tensor_scales_and_softmax_scale():
     G.layer_parity(w)
 
 
+def test_negative_k_tensor_scale():
+    # the sign of the score scale moves into Q: the softmax max is still the
+    # max of the scaled scores
+    w = make_workload("neg_scale", 35, [1500, 300], 2, 16, 2, 4, KV_NVFP4, IDX_FP8, table="permute",
+                      k_tensor_scale=-0.5)
+    G.layer_parity(w)
+
+
 def test_top_k_and_keep_last_variants():
     for k, keep in ((4, 1), (16, 0), (1, 1)):
         w = make_workload("k%d_keep%d" % (k, keep), 34, [3000, 700], 1, 8, 1, 3, KV_NVFP4, IDX_FP8,

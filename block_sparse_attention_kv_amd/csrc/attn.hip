@@ -10,7 +10,10 @@
 // inside the sparse-attention kernels.]
 //
 // Work split. One workgroup per (sequence, query token, KV head) with W
-// wavefronts. In the fused decode layer the workgroup first picks its query
+// wavefronts; for small bf16 batches S = 4 workgroups per item each take a
+// quarter of the selected blocks (one per wave), publish their softmax
+// states to the workspace, and the last to arrive merges them in a fixed
+// order. In the fused decode layer the workgroup first picks its query
 // token's blocks from the pooled scores (topk.hpp); the selection is cheap
 // next to the K/V traffic, so the KV heads of one token each repeat it rather
 // than wait for one another. Wave w then takes the selected blocks w, w+W, ...
@@ -159,11 +162,12 @@ __global__ __launch_bounds__(64 * W, (W <= 4 ? 2 : 1)) void sparse_attn_kernel(A
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];  // select / V-scale stages / merge
   __shared__ TopkLds tk;
   __shared__ int32_t sel_lds[kTopkMax], blist[kTopkMax], plist[kTopkMax];
-  __shared__ int32_t nlist;
+  __shared__ int32_t nlist, last_lds;
 
   const int tid = threadIdx.x, lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps block loops scalar
-  const int item = blockIdx.x;
+  const int item = blockIdx.x / a.splits;   // (sequence, token, KV head)
+  const int split = blockIdx.x % a.splits;  // this workgroup's share of the item's blocks
   const int g = item % a.Hkv;
   const int bt = item / a.Hkv;
   const int t = bt % a.Tq, b = bt / a.Tq;
@@ -200,7 +204,8 @@ __global__ __launch_bounds__(64 * W, (W <= 4 ? 2 : 1)) void sparse_attn_kernel(A
     nsel = a.top_k;
     __syncthreads();
   }
-  // blocks that exist, compacted, order kept
+  // blocks that exist, compacted, order kept; a split item keeps its share
+  // (split s of S: positions [s*per, (s+1)*per), per = ceil(count / S))
   if (wave == 0) {
     bool ok = false;
     int blk = -1, page = -1;
@@ -212,12 +217,14 @@ __global__ __launch_bounds__(64 * W, (W <= 4 ? 2 : 1)) void sparse_attn_kernel(A
       }
     }
     const uint64_t bal = __ballot(ok);
-    if (ok) {
-      const int pos = __popcll(bal & ((1ull << lane) - 1ull));
+    const int cnt = __popcll(bal);
+    const int per = (cnt + a.splits - 1) / a.splits, first = split * per;
+    const int pos = __popcll(bal & ((1ull << lane) - 1ull)) - first;
+    if (ok && pos >= 0 && pos < per) {
       blist[pos] = blk;
       plist[pos] = page;
     }
-    if (lane == 0) nlist = __popcll(bal);
+    if (lane == 0) nlist = max(0, min(per, cnt - first));
   }
 
   vec qb[4];
@@ -479,6 +486,62 @@ __global__ __launch_bounds__(64 * W, (W <= 4 ? 2 : 1)) void sparse_attn_kernel(A
     }
   }
 
+  if (a.splits > 1) {
+    // ---- split item: publish this workgroup's state; the last of the
+    // item's workgroups to arrive combines all of them in split order. The
+    // arrival word holds (epoch << 32) | count; a word from an older launch
+    // (another epoch) counts as zero, so the workspace needs no clearing.
+    float* mine = a.partials + ((size_t)item * a.splits + split) * (16 * kPartRow);
+    if (wave == 0) {
+#pragma unroll
+      for (int d = 0; d < 8; d++) *reinterpret_cast<f32x4*>(mine + h * kPartRow + 16 * d + 4 * q4) = st.o[d];
+      if (q4 == 0) {
+        mine[h * kPartRow + 128] = st.m;
+        mine[h * kPartRow + 129] = st.l;
+      }
+    }
+    __threadfence();  // release: the state is visible device-wide before the arrival
+    __syncthreads();
+    if (tid == 0) {
+      unsigned long long* word = a.arrivals + item;
+      const unsigned long long fresh = (unsigned long long)a.epoch << 32;
+      unsigned long long seen = __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), mine_cnt;
+      for (;;) {  // ends within `splits` rounds: every failure is another workgroup's success
+        const unsigned long long want = ((seen >> 32) == a.epoch ? seen : fresh) + 1ull;
+        const unsigned long long prev = atomicCAS(word, seen, want);
+        if (prev == seen) {
+          mine_cnt = want & 0xFFFFFFFFull;
+          break;
+        }
+        seen = prev;
+      }
+      last_lds = (int)mine_cnt == a.splits;
+    }
+    __syncthreads();
+    if (!last_lds) return;
+    __threadfence();  // acquire: the other workgroups' states
+    if (wave == 0) {
+      const float* all = a.partials + (size_t)item * a.splits * (16 * kPartRow);
+      float M = -INFINITY;
+      for (int sp = 0; sp < a.splits; sp++) M = fmaxf(M, all[sp * (16 * kPartRow) + h * kPartRow + 128]);
+      float l = 0.0f;
+      f32x4 o[8];
+#pragma unroll
+      for (int d = 0; d < 8; d++) o[d] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      for (int sp = 0; sp < a.splits; sp++) {
+        const float* row = all + sp * (16 * kPartRow) + h * kPartRow;
+        const float w = lse_weight(row[128], M);
+        l += w * row[129];
+#pragma unroll
+        for (int d = 0; d < 8; d++) o[d] += w * *reinterpret_cast<const f32x4*>(row + 16 * d + 4 * q4);
+      }
+      st.m = M;
+      st.l = l;
+#pragma unroll
+      for (int d = 0; d < 8; d++) st.o[d] = o[d];
+    }
+  }
+
   // ---- write bf16 output (and lse) for the real heads
   if (wave == 0 && h < a.grp) {
     const size_t row = (size_t)bt * a.Hq + g * a.grp + h;
@@ -509,7 +572,7 @@ size_t attn_lds_bytes(const AttnArgs& a, int W) {
 
 template <bool NVFP4>
 hipError_t launch_w(const AttnArgs& a, int waves, hipStream_t s, const KTimer* tm) {
-  const dim3 grid(a.B * a.Tq * a.Hkv);
+  const dim3 grid(a.B * a.Tq * a.Hkv * a.splits);
   const size_t lds = attn_lds_bytes(a, waves);
   switch (waves) {
     case 4: return launch_kernel(sparse_attn_kernel<NVFP4, 4>, grid, dim3(256), lds, s, a, tm);
@@ -522,6 +585,9 @@ hipError_t launch_w(const AttnArgs& a, int waves, hipStream_t s, const KTimer* t
 
 hipError_t launch_attn(const AttnArgs& a, bool nvfp4, int waves, hipStream_t s, const KTimer* tm) {
   if (a.top_k < 1 || a.top_k > kTopkMax || a.maxb < 1 || a.maxb > kSelectMaxBlocks) return hipErrorInvalidValue;
+  if (a.splits < 1 || a.splits > kTopkMax || (a.splits > 1 && (!a.partials || !a.arrivals)))
+    return hipErrorInvalidValue;
+  if (a.splits > 1) waves = 4;  // a split share is at most 4 blocks: one per wave
   return nvfp4 ? launch_w<true>(a, waves, s, tm) : launch_w<false>(a, waves, s, tm);
 }
 

@@ -6,6 +6,9 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <atomic>
+#include <chrono>
+
 #include "../../include/msa.h"
 #include "msa_internal.hpp"
 
@@ -94,16 +97,58 @@ msa_status_t check_cache_idx(const msa_params_t* p, const msa_cache_t* c) {
   return MSA_OK;
 }
 
-// Workspace of msa_decode_layer: the pooled block scores.
+// Workspace: the pooled block scores and, for small batches whose
+// attention items are split over several workgroups, the per-split softmax
+// states and one arrival word per item.
 struct Layout {
-  size_t pooled_off, total;
+  size_t pooled_off, part_off, arrive_off, total;
+  int splits;
 };
+// Only the bf16 path splits: its block loop has no prefetch, so a wave pays
+// the full load latency per block and one block per wave halves the chain.
+// The NVFP4 path prefetches the next block, and there the repeated fused
+// selection and the publish/combine of the states cost more than one fewer
+// block per wave saves (measured on the 32K and 512K workloads).
+int attn_splits(const msa_params_t* p) {
+  const int64_t items = (int64_t)p->num_seqs * p->q_len * p->num_kv_heads;
+  return (p->kv_dtype == MSA_KV_BF16 && items <= kAttnSplitMaxItems) ? kAttnSplits : 1;
+}
 Layout layout(const msa_params_t* p) {
   Layout L;
   const size_t bt = (size_t)p->num_seqs * p->q_len;
+  const size_t items = bt * p->num_kv_heads;
+  L.splits = attn_splits(p);
   L.pooled_off = 0;
-  L.total = align256(bt * p->max_blocks_per_seq * sizeof(float));
+  L.part_off = align256(bt * p->max_blocks_per_seq * sizeof(float));
+  const size_t part = L.splits > 1 ? items * L.splits * 16 * kPartRow * sizeof(float) : 0;
+  L.arrive_off = L.part_off + align256(part);
+  L.total = L.arrive_off + (L.splits > 1 ? align256(items * sizeof(unsigned long long)) : 0);
   return L;
+}
+
+// A distinct epoch per attention launch (arrival words of older launches
+// then read as zero); the start is drawn from the clock so that workspaces
+// reused across processes do not meet the same sequence.
+uint32_t next_epoch() {
+  static std::atomic<uint32_t> ctr{0};
+  static const uint32_t base = (uint32_t)std::chrono::steady_clock::now().time_since_epoch().count() * 2654435761u;
+  return base + ctr.fetch_add(1, std::memory_order_relaxed) + 1u;
+}
+
+// Splits the attention of small batches when the workspace has room.
+void set_splits(AttnArgs& a, const msa_params_t* p, void* workspace, size_t ws_bytes) {
+  const Layout L = layout(p);
+  a.splits = 1;
+  a.partials = nullptr;
+  a.arrivals = nullptr;
+  a.epoch = 0;
+  if (L.splits > 1 && workspace && ws_bytes >= L.total && (reinterpret_cast<uintptr_t>(workspace) & 255) == 0) {
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    a.splits = L.splits;
+    a.partials = reinterpret_cast<float*>(ws + L.part_off);
+    a.arrivals = reinterpret_cast<unsigned long long*>(ws + L.arrive_off);
+    a.epoch = next_epoch();
+  }
 }
 
 // Compute units of the current device (the persistent indexer grid is sized
@@ -178,6 +223,10 @@ AttnArgs attn_args(const msa_params_t* p, const msa_cache_t* c, const void* q, c
   const bool fp4 = p->kv_dtype == MSA_KV_NVFP4;
   a.score_scale = softmax_scale(p) * 1.4426950408889634f * (fp4 ? c->k_tensor_scale : 1.0f);
   a.v_scale_mul = fp4 ? c->v_tensor_scale : 1.0f;
+  a.partials = nullptr;
+  a.arrivals = nullptr;
+  a.epoch = 0;
+  a.splits = 1;
   a.B = p->num_seqs;
   a.Tq = p->q_len;
   a.Hq = p->num_q_heads;
@@ -248,13 +297,12 @@ msa_status_t msa_pool_select_blocks(const msa_params_t* p, const int32_t* ctx_le
 msa_status_t msa_sparse_attn_decode(const msa_params_t* p, const msa_cache_t* c, const void* q, const int32_t* sel,
                                     void* out, float* lse, void* workspace, size_t ws_bytes, void* stream) {
   g_err[0] = 0;
-  (void)workspace;
-  (void)ws_bytes;
   msa_status_t st = check_params(p);
   if (st != MSA_OK) return st;
   if ((st = check_cache_kv(p, c)) != MSA_OK) return st;
   if (!q || !sel || !out) return fail(MSA_ERR_INVALID_ARG, "q / sel / out is NULL");
   AttnArgs a = attn_args(p, c, q, nullptr, const_cast<int32_t*>(sel), out, lse);
+  set_splits(a, p, workspace, ws_bytes);
   hipError_t e = launch_attn(a, p->kv_dtype == MSA_KV_NVFP4, attn_waves(p), static_cast<hipStream_t>(stream));
   return e == hipSuccess ? MSA_OK : hip_fail(e, "attention launch");
 }
@@ -285,6 +333,7 @@ msa_status_t msa_decode_layer_traced(const msa_params_t* p, const msa_cache_t* c
 
   // selection (from the pooled scores) fused into the attention kernel
   AttnArgs aa = attn_args(p, c, q, pooled, sel_out, out, lse);
+  set_splits(aa, p, workspace, ws_bytes);
   e = launch_attn(aa, p->kv_dtype == MSA_KV_NVFP4, attn_waves(p), s, &t1);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   return MSA_OK;

@@ -28,6 +28,10 @@ constexpr int kIndexerMaxSeqs = 8192;
 // Selection: at most 16 blocks per query token; the pooled scores of one
 // token (at most 8192 blocks) are held in LDS.
 constexpr int kTopkMax = 16;
+// Split attention: per head, O[128], m, l and two pad floats (16-byte rows).
+constexpr int kPartRow = 132;
+constexpr int kAttnSplits = 4;         // workgroups per item for small batches
+constexpr int kAttnSplitMaxItems = 64; // items up to which the work is split
 constexpr int kSelectMaxBlocks = 8192;
 
 // Pool (optional) + top-k block selection per (sequence, query token).
@@ -58,6 +62,10 @@ struct AttnArgs {
   const uint8_t* v_scale;
   uint16_t* out;            // bf16 [B][Tq][Hq][128]
   float* lse;               // [B][Tq][Hq] or nullptr
+  float* partials;          // [items][splits][16][kPartRow] softmax states (splits > 1)
+  unsigned long long* arrivals;  // [items]: (epoch << 32) | workgroups arrived (splits > 1)
+  uint32_t epoch;           // distinct per call: older arrival words count as zero
+  int splits;               // workgroups per (sequence, token, KV head) item
   float score_scale;        // softmax_scale * log2(e) * k_tensor_scale
   float v_scale_mul;        // v_tensor_scale
   int B, Tq, Hq, Hkv, grp, maxb, num_pages, top_k, keep_last;

@@ -141,3 +141,23 @@ def test_decode_layer_traced_matches_plain():
     assert np.array_equal(sel.cpu().numpy(), plain["sel"])
     for i in range(msa.NUM_STAGES):
         assert evs[2 * i].elapsed_time(evs[2 * i + 1]) > 0.0
+
+
+def test_split_attention_reuses_workspace():
+    # small bf16 batches split every item over 4 workgroups that meet through
+    # arrival words in the workspace; repeated calls on the same workspace
+    # (words left by earlier calls) must give the same, correct result
+    w = small_cases()[1]
+    run = G.Run(w)
+    prm = w.params
+    B, Tq, Hq, K = prm["num_seqs"], prm["q_len"], prm["num_q_heads"], prm["top_k"]
+    ws = msa.alloc_workspace(run.params, "cuda")
+    outs = []
+    for _ in range(3):
+        out = torch.empty((B, Tq, Hq, 128), dtype=torch.int16, device="cuda")
+        sel = torch.empty((B, Tq, K), dtype=torch.int32, device="cuda")
+        msa.msa_decode_layer(run.params, run.cache, run.q, run.idx_q, run.idx_w, out, ws, sel_out=sel)
+        torch.cuda.synchronize()
+        outs.append((out.cpu().numpy(), sel.cpu().numpy()))
+    assert all(np.array_equal(o[0], outs[0][0]) and np.array_equal(o[1], outs[0][1]) for o in outs)
+    G.layer_parity(w, run=run)

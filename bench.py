@@ -36,7 +36,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(ROOT, "block_sparse_attention_kv_amd", "csrc")
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "traffic.json")
 # sources that define the indexer kernel's memory traffic
-INDEXER_SOURCES = ("indexer.hip", "fmt.hpp", "msa_internal.hpp")
+# the files the indexer kernel's device code is compiled from (the host-side
+# launch helpers it also includes do not change the kernel)
+INDEXER_SOURCES = ("indexer.hip", "fmt.hpp", "indexer_args.hpp")
 
 
 def log(*a):

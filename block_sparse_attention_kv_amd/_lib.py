@@ -78,6 +78,7 @@ def load():
         "msa_sparse_attn_decode": (st, [P, C, vp, vp, vp, vp, vp, sz, vp]),
         "msa_decode_layer": (st, [P, C, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
         "msa_decode_layer_traced": (st, [P, C, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp]),
+        "msa_decode_layer_single": (st, [P, C, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
         "msa_kv_insert": (st, [P, C, vp, vp, vp, vp]),
         "msa_debug_dequant_nvfp4": (st, [vp, vp, i64, vp, vp]),
         "msa_debug_dequant_fp8": (st, [vp, i64, vp, vp]),
@@ -94,7 +95,7 @@ def load():
 
 
 EXPORTED = ("msa_workspace_size", "msa_indexer_scores", "msa_pool_select_blocks", "msa_sparse_attn_decode",
-            "msa_decode_layer", "msa_decode_layer_traced", "msa_kv_insert", "msa_debug_dequant_nvfp4",
+            "msa_decode_layer", "msa_decode_layer_traced", "msa_decode_layer_single", "msa_kv_insert", "msa_debug_dequant_nvfp4",
             "msa_debug_dequant_fp8",
             "msa_status_string", "msa_last_error", "msa_version")
 
@@ -216,6 +217,16 @@ def msa_decode_layer(params, cache, q, idx_q, idx_w, out, workspace, lse=None, s
                                        _ptr(out), _ptr(lse), _ptr(sel_out), _ptr(workspace), ws_bytes,
                                        _stream(stream), arr)
     _check(st, "msa_decode_layer")
+
+
+def msa_decode_layer_single(params, cache, q, idx_q, idx_w, out, workspace, lse=None, sel_out=None, stream=None):
+    """msa_decode_layer in one cooperative kernel launch (NVFP4 K/V, FP8 or
+    NVFP4 indexer keys, q_len <= 4)."""
+    c = cache.c()
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(load().msa_decode_layer_single(ctypes.byref(params), ctypes.byref(c), _ptr(q), _ptr(idx_q), _ptr(idx_w),
+                                          _ptr(out), _ptr(lse), _ptr(sel_out), _ptr(workspace), ws_bytes,
+                                          _stream(stream)), "msa_decode_layer_single")
 
 
 def msa_kv_insert(params, cache, new_k, new_v, new_idx_k, stream=None):

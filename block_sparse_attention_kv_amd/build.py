@@ -37,8 +37,10 @@ def hipcc():
 
 # Per-file flags. The indexer keeps matrix-core results in VGPRs (its
 # accumulators are consumed at once by vector code; the AGPR round trip costs
-# one extra instruction per element).
-FILE_FLAGS = {"indexer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# one extra instruction per element); so does the single-launch layer, which
+# holds the indexer's code.
+FILE_FLAGS = {"indexer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+              "layer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def sources():

@@ -1,0 +1,536 @@
+// attn_impl.hpp -- device code of the MSA sparse attention (gfx950); the
+// design is described at the top of attn.hip. Used by the attention kernel
+// and by the single-launch decode layer.
+#pragma once
+#include "fmt.hpp"
+#include "msa_internal.hpp"
+#include "topk.hpp"
+
+namespace msa {
+
+namespace {
+
+
+constexpr int kSlotFloats = 16 * kHeadDim + 32;  // O[16][128], m[16], l[16]
+
+__device__ __forceinline__ int kappa(int tau, int rho) {
+  return 32 * (rho >> 2) + 8 * (tau >> 1) + 4 * (tau & 1) + (rho & 3);
+}
+// kappa(tau, rho) = krow(rho) + ktau(tau)
+__host__ __device__ constexpr int ktau(int tau) { return 8 * (tau >> 1) + 4 * (tau & 1); }
+
+template <bool NVFP4>
+struct MfmaT;
+template <>
+struct MfmaT<true> {
+  typedef f16x8 vec;
+  static __device__ __forceinline__ f32x4 mma(vec a, vec b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ uint32_t pack(float x, float y) { return f32x2_to_f16x2(x, y); }
+  // acc + both halves of a packed pair (v_dot2_f32_f16 against ones)
+  static __device__ __forceinline__ float sum2(uint32_t p, float acc) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, p), f16x2{(f16)1.0f, (f16)1.0f}, acc, false);
+  }
+};
+template <>
+struct MfmaT<false> {
+  typedef bf16x8 vec;
+  static __device__ __forceinline__ f32x4 mma(vec a, vec b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ uint32_t pack(float x, float y) { return f32x2_to_bf16x2(x, y); }
+  static __device__ __forceinline__ float sum2(uint32_t p, float acc) {
+    return acc + bf16_bits_to_f32(p & 0xFFFFu) + bf16_bits_to_f32(p >> 16);
+  }
+};
+
+struct SoftmaxState {
+  float m;       // running max (log2 domain), per head
+  float l;       // this lane's share of the running sum
+  f32x4 o[8];    // O^T tile delta: dims 16*delta + 4*(lane/16) + r, head lane%16
+};
+
+__device__ __forceinline__ float lse_weight(float m, float M) {
+  return (m == -INFINITY) ? 0.0f : fast_exp2(m - M);
+}
+
+// ---------------------------------------------------------------- NVFP4 I/O
+
+// Buffer resources of one block of one KV head (K codes, K scales, V codes,
+// V scales); empty ranges when `none`.
+struct KvRsrc {
+  __amdgpu_buffer_rsrc_t kd, ks, vd, vs;
+};
+__device__ __forceinline__ KvRsrc nvfp4_rsrc(const AttnArgs& a, int page, int g, bool none) {
+  const size_t pg = (size_t)(none ? 0 : page) * a.Hkv + g;
+  const uint32_t n8k = none ? 0u : 8192u, n1k = none ? 0u : 1024u;
+  KvRsrc r;
+  r.kd = make_rsrc(a.k_data + pg * 8192, n8k);
+  r.ks = make_rsrc(a.k_scale + pg * 1024, n1k);
+  r.vd = make_rsrc(a.v_data + pg * 8192, n8k);
+  r.vs = make_rsrc(a.v_scale + pg * 1024, n1k);
+  return r;
+}
+
+// This lane's share of a block: K codes of key kappa(tau, l%16), dims
+// 32*(l/16) .. +31 (16 bytes), and the two E4M3 scales of those dims; V codes
+// of dim 16*dt + l%16, tokens 32*(l/16) .. +31, and 16 bytes of the [8][128]
+// V scale array.
+struct KRegs {
+  u32x4 kd[8];
+  uint32_t ks[8];
+};
+struct VRegs {
+  u32x4 vd[8];
+  u32x4 vs;
+};
+struct LaneOff {
+  uint32_t k, ks, v, vs;
+};
+
+__device__ __forceinline__ void load_k(const KvRsrc& r, const LaneOff& o, KRegs& K) {
+#pragma unroll
+  for (int tau = 0; tau < 8; tau++) {
+    K.kd[tau] = buf_load16<kAuxNT>(r.kd, o.k, (uint32_t)(64 * ktau(tau)));
+    K.ks[tau] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r.ks, (int)o.ks, 8 * ktau(tau), kAuxNT);
+  }
+}
+__device__ __forceinline__ void load_v(const KvRsrc& r, const LaneOff& o, VRegs& V) {
+#pragma unroll
+  for (int dt = 0; dt < 8; dt++) V.vd[dt] = buf_load16<kAuxNT>(r.vd, o.v, (uint32_t)(1024 * dt));
+  V.vs = buf_load16<kAuxNT>(r.vs, o.vs, 0);
+}
+
+// ---------------------------------------------------------------- kernel
+
+// The attention of workgroup wg (item wg / splits, share wg % splits) with
+// W waves; lds: the dynamic LDS region (attn_lds_bytes); tid: threadIdx.x
+// (a caller that loops over items passes it through an empty asm statement,
+// so that the lane-dependent set-up is redone per item instead of being
+// hoisted and held in registers across the loop). COHERENT: read the pooled
+// scores with device-scope relaxed atomic loads (written by the same grid).
+// Every thread of the workgroup calls it.
+template <bool NVFP4, int W, bool COHERENT = false>
+__device__ __forceinline__ void attn_body(const AttnArgs& a, int wg, uint8_t* lds, int tid) {
+  typedef MfmaT<NVFP4> MT;
+  typedef typename MT::vec vec;
+  constexpr int NT = 64 * W;
+  __shared__ TopkLds tk;
+  __shared__ int32_t sel_lds[kTopkMax], blist[kTopkMax], plist[kTopkMax];
+  __shared__ int32_t nlist, last_lds;
+
+  const int lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps block loops scalar
+  const int item = wg / a.splits;   // (sequence, token, KV head)
+  const int split = wg % a.splits;  // this workgroup's share of the item's blocks
+  const int g = item % a.Hkv;
+  const int bt = item / a.Hkv;
+  const int t = bt % a.Tq, b = bt / a.Tq;
+  const int Lc = clamp_ctx(a.ctx_lens[b], a.maxb);
+  const int p = Lc - a.Tq + t;  // last visible key
+  const int h = lane & 15;      // head within the group (MFMA column)
+  const int q4 = lane >> 4;     // lane group 0..3
+
+  // ---- Q^T operand: head h, dims 32*q4 + 8s + e (issued before the
+  // selection; it does not depend on it)
+  u32x4 qraw[4];
+  {
+    const bool ok = h < a.grp;
+    const uint16_t* qrow = a.q + ((size_t)bt * a.Hq + g * a.grp + h) * kHeadDim + 32 * q4;
+#pragma unroll
+    for (int s = 0; s < 4; s++) qraw[s] = ok ? reinterpret_cast<const u32x4*>(qrow)[s] : u32x4{0, 0, 0, 0};
+  }
+
+  // ---- selected blocks (fused: from the pooled scores; the block-table
+  // entries of all visible blocks are fetched in the same pass into an LDS
+  // page table, so the winners' pages need no second dependent load)
+  int nsel;
+  int32_t* pages = reinterpret_cast<int32_t*>(lds);  // [nvis], fused path only
+  const int32_t* bt_row = a.block_table + (size_t)b * a.maxb;
+  if (a.pooled) {
+    const int nvis = p < 0 ? 0 : p / kBlock + 1;
+    const float* src = a.pooled + (size_t)bt * a.maxb;
+    nsel = block_topk<NT>(
+        [&](int i) {
+          if constexpr (COHERENT) return __hip_atomic_load(src + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          else return src[i];
+        },
+        [&](int i) { return bt_row[i]; }, pages, nvis,
+                          a.top_k, a.keep_last != 0, sel_lds, tk);
+    if (g == 0 && a.sel)
+      for (int k = tid; k < a.top_k; k += NT) a.sel[(size_t)bt * a.top_k + k] = k < nsel ? sel_lds[k] : -1;
+  } else {
+    if (tid < a.top_k) sel_lds[tid] = a.sel[(size_t)bt * a.top_k + tid];
+    nsel = a.top_k;
+    __syncthreads();
+  }
+  // blocks that exist, compacted, order kept; a split item keeps its share
+  // (split s of S: positions [s*per, (s+1)*per), per = ceil(count / S))
+  if (wave == 0) {
+    bool ok = false;
+    int blk = -1, page = -1;
+    if (lane < nsel && p >= 0) {
+      blk = sel_lds[lane];
+      if (blk >= 0 && blk < a.maxb && blk * kBlock <= p) {
+        page = a.pooled ? pages[blk] : bt_row[blk];
+        ok = page >= 0 && page < a.num_pages;
+      }
+    }
+    const uint64_t bal = __ballot(ok);
+    const int cnt = __popcll(bal);
+    const int per = (cnt + a.splits - 1) / a.splits, first = split * per;
+    const int pos = __popcll(bal & ((1ull << lane) - 1ull)) - first;
+    if (ok && pos >= 0 && pos < per) {
+      blist[pos] = blk;
+      plist[pos] = page;
+    }
+    if (lane == 0) nlist = max(0, min(per, cnt - first));
+  }
+
+  vec qb[4];
+  float cscale;
+  if constexpr (NVFP4) {
+    float amax = 0.0f;
+#pragma unroll
+    for (int s = 0; s < 4; s++)
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        const uint32_t w = qraw[s][e];
+        amax = fmaxf(amax, fmaxf(fabsf(bf16_bits_to_f32(w & 0xFFFFu)), fabsf(bf16_bits_to_f32(w >> 16))));
+      }
+    amax = fmaxf(amax, shfl_xor(amax, 16));
+    amax = fmaxf(amax, shfl_xor(amax, 32));
+    // power-of-two pre-scale keeping the row inside fp16's range
+    int sh = 0;
+    if (amax >= 32768.0f) sh = ((int)((__float_as_uint(amax) >> 23) & 255) - 127) - 14;
+    // the sign of the score scale (a negative K tensor scale) moves into Q,
+    // so that the softmax can take the max of the raw dot products
+    const float sgn = a.score_scale < 0.0f ? -1.0f : 1.0f;
+    const float down = sgn * __uint_as_float((uint32_t)(127 - sh) << 23);
+    cscale = fabsf(a.score_scale) * __uint_as_float((uint32_t)(127 + sh) << 23);
+#pragma unroll
+    for (int s = 0; s < 4; s++) {
+      u32x4 v;
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        const uint32_t w = qraw[s][e];
+        v[e] = f32x2_to_f16x2(bf16_bits_to_f32(w & 0xFFFFu) * down, bf16_bits_to_f32(w >> 16) * down);
+      }
+      qb[s] = __builtin_bit_cast(vec, v);
+    }
+  } else {
+    // bf16 Q is used as is; a negative score scale (negative K tensor scale)
+    // flips Q's sign bits so that the softmax sees a scale >= 0
+    const uint32_t flip = a.score_scale < 0.0f ? 0x80008000u : 0u;
+    cscale = fabsf(a.score_scale);
+#pragma unroll
+    for (int s = 0; s < 4; s++) qb[s] = __builtin_bit_cast(vec, qraw[s] ^ flip);
+  }
+  __syncthreads();
+  const int n = __builtin_amdgcn_readfirstlane(nlist);
+
+  SoftmaxState st;
+  st.m = -INFINITY;
+  st.l = 0.0f;
+#pragma unroll
+  for (int d = 0; d < 8; d++) st.o[d] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  // raw scores of one block (S^T tiles) -> online softmax update and the P^T
+  // operand. cscale >= 0, so the max of the scaled scores is cscale times the
+  // max of the raw ones.
+  auto softmax_update = [&](f32x4 (&sacc)[8], float rmax, bool masked, vec (&pb)[4]) {
+    rmax = fmaxf(rmax, shfl_xor(rmax, 16));
+    rmax = fmaxf(rmax, shfl_xor(rmax, 32));
+    const float bmax = rmax == -INFINITY ? -INFINITY : rmax * cscale;
+    const float mnew = fmaxf(st.m, bmax);
+    float psum = 0.0f;
+#pragma unroll
+    for (int s = 0; s < 4; s++) {
+      float pv[8];
+#pragma unroll
+      for (int e = 0; e < 8; e++) {
+        const float x = sacc[2 * s + (e >> 2)][e & 3];
+        float v = fast_exp2(fmaf(x, cscale, -mnew));
+        if (masked) v = x == -INFINITY ? 0.0f : v;
+        pv[e] = v;
+      }
+      u32x4 pk;
+      pk.x = MT::pack(pv[0], pv[1]);
+      pk.y = MT::pack(pv[2], pv[3]);
+      pk.z = MT::pack(pv[4], pv[5]);
+      pk.w = MT::pack(pv[6], pv[7]);
+      pb[s] = __builtin_bit_cast(vec, pk);
+      // the row sum takes the same rounded P that multiplies V
+#pragma unroll
+      for (int e = 0; e < 4; e++) psum = MT::sum2(pk[e], psum);
+    }
+    // rescale the running state only if some head's max grew
+    if (__ballot(mnew != st.m) != 0) {
+      const float alpha = lse_weight(st.m, mnew);
+      st.l *= alpha;
+#pragma unroll
+      for (int d = 0; d < 8; d++) st.o[d] *= alpha;
+    }
+    st.l += psum;
+    st.m = mnew;
+  };
+  // The block holding keys past p (the context's last block) takes the masked
+  // path; the two paths are whole branches so that full blocks do not pay for
+  // the mask.
+  auto softmax_block = [&](f32x4 (&sacc)[8], int blk, bool partial, vec (&pb)[4]) {
+    if (partial) {
+      float rmax = -INFINITY;
+#pragma unroll
+      for (int tau = 0; tau < 8; tau++)
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+          const bool vis = blk * kBlock + kappa(tau, 4 * q4 + r) <= p;
+          sacc[tau][r] = vis ? sacc[tau][r] : -INFINITY;
+          rmax = fmaxf(rmax, sacc[tau][r]);
+        }
+      softmax_update(sacc, rmax, true, pb);
+    } else {
+      float rmax = -INFINITY;
+#pragma unroll
+      for (int tau = 0; tau < 8; tau++)
+#pragma unroll
+        for (int r = 0; r < 4; r++) rmax = fmaxf(rmax, sacc[tau][r]);
+      softmax_update(sacc, rmax, false, pb);
+    }
+  };
+
+  if constexpr (NVFP4) {
+    // fp16 V scales of the current block: [8 groups][128 keys] per wave
+    f16* vs_stage = reinterpret_cast<f16*>(lds) + wave * 1024;
+    const int rho = lane & 15;
+    LaneOff off;
+    off.k = (uint32_t)((32 * (rho >> 2) + (rho & 3)) * 64 + 16 * q4);
+    off.ks = (uint32_t)((32 * (rho >> 2) + (rho & 3)) * 8 + 2 * q4);
+    off.v = (uint32_t)(rho * 64 + 16 * q4);
+    off.vs = (uint32_t)(16 * lane);
+    KRegs K;
+    VRegs V;
+    {
+      const bool none = wave >= n;
+      const int pg = none ? 0 : __builtin_amdgcn_readfirstlane(plist[wave]);
+      const KvRsrc r0 = nvfp4_rsrc(a, pg, g, none);
+      load_k(r0, off, K);
+      load_v(r0, off, V);
+    }
+    // Fully unrolled over the wave's at most kTopkMax / W blocks: straight-line
+    // code keeps the compiler's load counters exact across blocks (a loop
+    // header merges the first and later iterations' load orders and makes
+    // every block wait for all outstanding loads). Iterations past the wave's
+    // last block run on empty resources and skip the softmax and P.V.
+#pragma unroll
+    for (int it = 0; it < kTopkMax / W; it++) {
+      const int i = wave + it * W;
+      const bool valid = i < n;
+      const int blk = valid ? __builtin_amdgcn_readfirstlane(blist[i]) : 0;
+      const bool none = i + W >= n;
+      const int pgn = none ? 0 : __builtin_amdgcn_readfirstlane(plist[i + W]);
+      const KvRsrc rn = nvfp4_rsrc(a, pgn, g, none);
+
+      // ---- S^T = K Q^T, then the next block's K
+      f32x4 sacc[8];
+#pragma unroll
+      for (int tau = 0; tau < 8; tau++) {
+        const uint32_t sc2 = fp8x2_f16x2<false>(K.ks[tau]);  // groups 2*q4, 2*q4+1
+        const uint32_t slo = bcast_lo16(sc2), shi = bcast_hi16(sc2);
+        f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int s = 0; s < 4; s++) {
+          const u32x4 kv = nvfp4x8_f16(K.kd[tau][s], s < 2 ? slo : shi);
+          acc = MT::mma(__builtin_bit_cast(vec, kv), qb[s], acc);
+        }
+        sacc[tau] = acc;
+      }
+      if (it + 1 < kTopkMax / W) load_k(rn, off, K);
+
+      if (valid) {
+        // ---- V scales to fp16 in LDS (wave-private)
+        {
+          const u32x4 lo = fp8x8_f16(V.vs.x, V.vs.y), hi = fp8x8_f16(V.vs.z, V.vs.w);
+          u32x4* dst = reinterpret_cast<u32x4*>(vs_stage + 16 * lane);
+          dst[0] = lo;
+          dst[1] = hi;
+          wave_lds_sync();
+        }
+
+        // ---- online softmax
+        vec pb[4];
+        softmax_block(sacc, blk, blk * kBlock + kBlock - 1 > p, pb);
+
+        // ---- O^T += V^T P^T; the scales of dim tile dt+1 are read while
+        // tile dt is decoded and multiplied
+        u32x4 sc[4], scn[4];
+#pragma unroll
+        for (int s = 0; s < 4; s++) sc[s] = *reinterpret_cast<const u32x4*>(vs_stage + 32 * q4 + 8 * s);
+#pragma unroll
+        for (int dt = 0; dt < 8; dt++) {
+          if (dt + 1 < 8) {
+#pragma unroll
+            for (int s = 0; s < 4; s++)
+              scn[s] = *reinterpret_cast<const u32x4*>(vs_stage + (dt + 1) * 128 + 32 * q4 + 8 * s);
+          }
+#pragma unroll
+          for (int s = 0; s < 4; s++) {
+            const u32x4 vv = nvfp4x8_f16_each(V.vd[dt][s], sc[s]);
+            st.o[dt] = MT::mma(__builtin_bit_cast(vec, vv), pb[s], st.o[dt]);
+          }
+#pragma unroll
+          for (int s = 0; s < 4; s++) sc[s] = scn[s];
+        }
+        wave_lds_sync();  // the stage is overwritten by the next block
+      }
+      if (it + 1 < kTopkMax / W) load_v(rn, off, V);
+    }
+  } else {
+    for (int i = wave; i < n; i += W) {
+      const int blk = __builtin_amdgcn_readfirstlane(blist[i]);
+      const size_t pg = (size_t)__builtin_amdgcn_readfirstlane(plist[i]) * a.Hkv + g;
+      const int rho = lane & 15;
+      const uint16_t* kb = reinterpret_cast<const uint16_t*>(a.k_data) + pg * (kBlock * kHeadDim);
+      f32x4 sacc[8];
+#pragma unroll
+      for (int tau = 0; tau < 8; tau++) {
+        const u32x4* kr = reinterpret_cast<const u32x4*>(kb + kappa(tau, rho) * kHeadDim + 32 * q4);
+        f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int s = 0; s < 4; s++) acc = MT::mma(__builtin_bit_cast(vec, kr[s]), qb[s], acc);
+        sacc[tau] = acc;
+      }
+      vec pb[4];
+      softmax_block(sacc, blk, blk * kBlock + kBlock - 1 > p, pb);
+      const uint16_t* vb = reinterpret_cast<const uint16_t*>(a.v_data) + pg * (kHeadDim * kBlock);
+#pragma unroll
+      for (int dt = 0; dt < 8; dt++) {
+        const u32x4* vr = reinterpret_cast<const u32x4*>(vb + (16 * dt + rho) * kBlock + 32 * q4);
+#pragma unroll
+        for (int s = 0; s < 4; s++) st.o[dt] = MT::mma(__builtin_bit_cast(vec, vr[s]), pb[s], st.o[dt]);
+      }
+    }
+  }
+
+  // ---- full row sum of this wave (the 4 lanes of a head)
+  st.l += shfl_xor(st.l, 16);
+  st.l += shfl_xor(st.l, 32);
+
+  // ---- merge the W wave states: fixed tree, LDS slots
+  float* slots = reinterpret_cast<float*>(lds);
+#pragma unroll
+  for (int step = W / 2; step >= 1; step >>= 1) {
+    __syncthreads();
+    if (wave >= step && wave < 2 * step) {
+      float* sl = slots + (wave - step) * kSlotFloats;
+#pragma unroll
+      for (int d = 0; d < 8; d++) *reinterpret_cast<f32x4*>(sl + h * kHeadDim + 16 * d + 4 * q4) = st.o[d];
+      if (q4 == 0) {
+        sl[16 * kHeadDim + h] = st.m;
+        sl[16 * kHeadDim + 16 + h] = st.l;
+      }
+    }
+    __syncthreads();
+    if (wave < step) {
+      const float* sl = slots + wave * kSlotFloats;
+      const float m2 = sl[16 * kHeadDim + h], l2 = sl[16 * kHeadDim + 16 + h];
+      const float M = fmaxf(st.m, m2);
+      const float a1 = lse_weight(st.m, M), a2 = lse_weight(m2, M);
+#pragma unroll
+      for (int d = 0; d < 8; d++) {
+        const f32x4 o2 = *reinterpret_cast<const f32x4*>(sl + h * kHeadDim + 16 * d + 4 * q4);
+        st.o[d] = st.o[d] * a1 + o2 * a2;
+      }
+      st.l = st.l * a1 + l2 * a2;
+      st.m = M;
+    }
+  }
+
+  if (a.splits > 1) {
+    // ---- split item: publish this workgroup's state; the last of the
+    // item's workgroups to arrive combines all of them in split order. The
+    // arrival word holds (epoch << 32) | count; a word from an older launch
+    // (another epoch) counts as zero, so the workspace needs no clearing.
+    float* mine = a.partials + ((size_t)item * a.splits + split) * (16 * kPartRow);
+    if (wave == 0) {
+#pragma unroll
+      for (int d = 0; d < 8; d++) *reinterpret_cast<f32x4*>(mine + h * kPartRow + 16 * d + 4 * q4) = st.o[d];
+      if (q4 == 0) {
+        mine[h * kPartRow + 128] = st.m;
+        mine[h * kPartRow + 129] = st.l;
+      }
+    }
+    __threadfence();  // release: the state is visible device-wide before the arrival
+    __syncthreads();
+    if (tid == 0) {
+      unsigned long long* word = a.arrivals + item;
+      const unsigned long long fresh = (unsigned long long)a.epoch << 32;
+      unsigned long long seen = __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), mine_cnt;
+      for (;;) {  // ends within `splits` rounds: every failure is another workgroup's success
+        const unsigned long long want = ((seen >> 32) == a.epoch ? seen : fresh) + 1ull;
+        const unsigned long long prev = atomicCAS(word, seen, want);
+        if (prev == seen) {
+          mine_cnt = want & 0xFFFFFFFFull;
+          break;
+        }
+        seen = prev;
+      }
+      last_lds = (int)mine_cnt == a.splits;
+    }
+    __syncthreads();
+    if (!last_lds) return;
+    __threadfence();  // acquire: the other workgroups' states
+    if (wave == 0) {
+      const float* all = a.partials + (size_t)item * a.splits * (16 * kPartRow);
+      float M = -INFINITY;
+      for (int sp = 0; sp < a.splits; sp++) M = fmaxf(M, all[sp * (16 * kPartRow) + h * kPartRow + 128]);
+      float l = 0.0f;
+      f32x4 o[8];
+#pragma unroll
+      for (int d = 0; d < 8; d++) o[d] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      for (int sp = 0; sp < a.splits; sp++) {
+        const float* row = all + sp * (16 * kPartRow) + h * kPartRow;
+        const float w = lse_weight(row[128], M);
+        l += w * row[129];
+#pragma unroll
+        for (int d = 0; d < 8; d++) o[d] += w * *reinterpret_cast<const f32x4*>(row + 16 * d + 4 * q4);
+      }
+      st.m = M;
+      st.l = l;
+#pragma unroll
+      for (int d = 0; d < 8; d++) st.o[d] = o[d];
+    }
+  }
+
+  // ---- write bf16 output (and lse) for the real heads
+  if (wave == 0 && h < a.grp) {
+    const size_t row = (size_t)bt * a.Hq + g * a.grp + h;
+    const bool empty = !(st.l > 0.0f);
+    const float inv = empty ? 0.0f : a.v_scale_mul / st.l;
+    uint16_t* orow = a.out + row * kHeadDim;
+#pragma unroll
+    for (int d = 0; d < 8; d++) {
+      const f32x4 o = st.o[d];
+      uint2 pk;
+      pk.x = f32x2_to_bf16x2(o[0] * inv, o[1] * inv);
+      pk.y = f32x2_to_bf16x2(o[2] * inv, o[3] * inv);
+      *reinterpret_cast<uint2*>(orow + 16 * d + 4 * q4) = pk;
+    }
+    if (a.lse && q4 == 0) a.lse[row] = empty ? -INFINITY : (st.m + __log2f(st.l)) * 0.69314718055994530942f;
+  }
+}
+
+// Dynamic LDS: the pooled scores of one token (fused selection), the
+// per-wave V-scale stages, and the merge slots reuse one region.
+inline size_t attn_lds_bytes(const AttnArgs& a, int W) {
+  size_t sel = a.pooled ? (size_t)a.maxb * sizeof(int32_t) : 0;  // page table
+  size_t stage = (size_t)W * 1024 * 2;
+  size_t merge = (size_t)(W / 2) * kSlotFloats * 4;
+  size_t m = sel > stage ? sel : stage;
+  return m > merge ? m : merge;
+}
+
+}  // namespace
+
+}  // namespace msa

@@ -97,11 +97,12 @@ msa_status_t check_cache_idx(const msa_params_t* p, const msa_cache_t* c) {
   return MSA_OK;
 }
 
-// Workspace: the pooled block scores and, for small batches whose
-// attention items are split over several workgroups, the per-split softmax
-// states and one arrival word per item.
+// Workspace: the pooled block scores, the completion flags of the indexer
+// workgroups (the single-launch layer) and, for small batches whose attention items are
+// split over several workgroups, the per-split softmax states and one
+// arrival word per item.
 struct Layout {
-  size_t pooled_off, part_off, arrive_off, total;
+  size_t pooled_off, done_off, part_off, arrive_off, total;
   int splits;
 };
 // Only the bf16 path splits: its block loop has no prefetch, so a wave pays
@@ -119,7 +120,8 @@ Layout layout(const msa_params_t* p) {
   const size_t items = bt * p->num_kv_heads;
   L.splits = attn_splits(p);
   L.pooled_off = 0;
-  L.part_off = align256(bt * p->max_blocks_per_seq * sizeof(float));
+  L.done_off = align256(bt * p->max_blocks_per_seq * sizeof(float));
+  L.part_off = L.done_off + align256((size_t)kLayerMaxIdxWgs * sizeof(uint32_t));
   const size_t part = L.splits > 1 ? items * L.splits * 16 * kPartRow * sizeof(float) : 0;
   L.arrive_off = L.part_off + align256(part);
   L.total = L.arrive_off + (L.splits > 1 ? align256(items * sizeof(unsigned long long)) : 0);
@@ -343,6 +345,34 @@ msa_status_t msa_decode_layer(const msa_params_t* p, const msa_cache_t* c, const
                               const float* idx_w, void* out, float* lse, int32_t* sel_out, void* workspace,
                               size_t ws_bytes, void* stream) {
   return msa_decode_layer_traced(p, c, q, idx_q, idx_w, out, lse, sel_out, workspace, ws_bytes, stream, nullptr);
+}
+
+msa_status_t msa_decode_layer_single(const msa_params_t* p, const msa_cache_t* c, const void* q, const void* idx_q,
+                                     const float* idx_w, void* out, float* lse, int32_t* sel_out, void* workspace,
+                                     size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  msa_status_t st = check_params(p);
+  if (st != MSA_OK) return st;
+  if (p->kv_dtype != MSA_KV_NVFP4 || (p->idx_dtype != MSA_IDX_FP8_E4M3 && p->idx_dtype != MSA_IDX_NVFP4) ||
+      p->q_len > 4)
+    return fail(MSA_ERR_UNSUPPORTED, "single-launch layer: NVFP4 K/V, FP8 or NVFP4 indexer keys, q_len <= 4");
+  if ((st = check_cache_kv(p, c)) != MSA_OK) return st;
+  if ((st = check_cache_idx(p, c)) != MSA_OK) return st;
+  if (!q || !idx_q || !idx_w || !out) return fail(MSA_ERR_INVALID_ARG, "q / idx_q / idx_w / out is NULL");
+  const Layout L = layout(p);
+  if (!workspace) return fail(MSA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", L.total);
+  if (ws_bytes < L.total) return fail(MSA_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, L.total);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
+    return fail(MSA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  float* pooled = reinterpret_cast<float*>(ws + L.pooled_off);
+  IndexerArgs ia = indexer_args(p, c, idx_q, idx_w);
+  ia.pooled = pooled;
+  AttnArgs aa = attn_args(p, c, q, pooled, sel_out, out, lse);
+  set_splits(aa, p, nullptr, 0);  // one workgroup per item
+  hipError_t e = launch_layer_single(ia, aa, reinterpret_cast<uint32_t*>(ws + L.done_off), next_epoch(),
+                                     p->idx_dtype, p->idx_heads <= 4 ? 4 : 8, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MSA_OK : hip_fail(e, "single-launch layer");
 }
 
 msa_status_t msa_kv_insert(const msa_params_t* p, const msa_cache_t* c, const void* new_k, const void* new_v,

@@ -101,6 +101,12 @@ hipError_t launch_indexer(const IndexerArgs& a, int key_format, int hp, hipStrea
 hipError_t launch_select(const SelectArgs& a, hipStream_t s);
 hipError_t launch_insert(const InsertArgs& a, hipStream_t s);
 hipError_t launch_attn(const AttnArgs& a, bool nvfp4, int waves, hipStream_t s, const KTimer* t = nullptr);
+// The decode layer as one launch (layer.hip); NVFP4 K/V, FP8 or NVFP4
+// indexer keys, q_len <= 4. wg_done: kLayerMaxIdxWgs flag words; epoch:
+// distinct per call.
+constexpr int kLayerMaxIdxWgs = 4096;
+hipError_t launch_layer_single(const IndexerArgs& ia, const AttnArgs& aa, uint32_t* wg_done, uint32_t epoch,
+                               int key_format, int hp, hipStream_t s, const KTimer* t = nullptr);
 hipError_t launch_debug_nvfp4(const uint8_t* codes, const uint8_t* scales, int64_t n_groups,
                               float* out, hipStream_t s);
 hipError_t launch_debug_fp8(const uint8_t* codes, int64_t n, float* out, hipStream_t s);

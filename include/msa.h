@@ -234,6 +234,26 @@ msa_status_t msa_decode_layer_traced(const msa_params_t* p, const msa_cache_t* c
                                      void* workspace, size_t ws_bytes, void* stream,
                                      void* const* stage_events);
 
+/* msa_decode_layer as ONE kernel launch on `stream` [upstreambeat page
+ * "vLLM turns MiniMax's day-zero promise into GPU-specific serving code",
+ * section "What changed": a single-launch ("mono") decode path on MI355X to
+ * cut launch overhead]: the indexer and pooling phase, a grid-wide barrier,
+ * then selection and attention. Same arguments, workspace and selection as
+ * msa_decode_layer; its attention always runs 4 waves per (sequence, token,
+ * KV head), so out and lse equal msa_decode_layer's bit for bit when the
+ * batch has at least two such items per compute unit (below that,
+ * msa_decode_layer spreads an item over 8 waves and the rounding of the
+ * merge differs). The grid is cooperative (two workgroups per
+ * compute unit, all resident at once), so it must not share the device with
+ * work that keeps those slots busy, and a device without cooperative launch
+ * returns MSA_ERR_HIP. Supported: kv_dtype MSA_KV_NVFP4, idx_dtype
+ * MSA_IDX_FP8_E4M3 or MSA_IDX_NVFP4, q_len <= 4; other valid problems return
+ * MSA_ERR_UNSUPPORTED before anything is enqueued. */
+msa_status_t msa_decode_layer_single(const msa_params_t* p, const msa_cache_t* cache,
+                                     const void* q, const void* idx_q, const float* idx_w,
+                                     void* out, float* lse, int32_t* sel_out,
+                                     void* workspace, size_t ws_bytes, void* stream);
+
 /* KV-insert: quantise the q_len new tokens of every sequence and write them
  * into the paged caches -- the step that precedes the decode of those tokens
  * [ainewsbites page "vLLM Adds Day-0 Support for MiniMax-M3.1-Flash on NVIDIA

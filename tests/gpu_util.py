@@ -53,15 +53,16 @@ class Run:
         self.shape_out = (B, Tq, Hq, 128)
         self.device = device
 
-    def layer(self, want_lse=True):
+    def layer(self, want_lse=True, single=False):
+        """msa_decode_layer, or msa_decode_layer_single when single."""
         prm = self.w.params
         B, Tq, Hq, K = prm["num_seqs"], prm["q_len"], prm["num_q_heads"], prm["top_k"]
         out = torch.empty(self.shape_out, dtype=torch.int16, device=self.device)
         lse = torch.empty((B, Tq, Hq), dtype=torch.float32, device=self.device) if want_lse else None
         sel = torch.empty((B, Tq, K), dtype=torch.int32, device=self.device)
         ws = msa.alloc_workspace(self.params, self.device)
-        msa.msa_decode_layer(self.params, self.cache, self.q, self.idx_q, self.idx_w, out, ws, lse=lse,
-                             sel_out=sel)
+        fn = msa.msa_decode_layer_single if single else msa.msa_decode_layer
+        fn(self.params, self.cache, self.q, self.idx_q, self.idx_w, out, ws, lse=lse, sel_out=sel)
         torch.cuda.synchronize()
         return dict(out=bf16_to_np(out), out_bits=out.cpu().numpy(), lse=None if lse is None else lse.cpu().numpy().astype(np.float64),
                     sel=sel.cpu().numpy())
@@ -188,12 +189,12 @@ def indexer_parity(w, run=None):
     return ties
 
 
-def layer_parity(w, run=None, seqs=None, tokens=None, strict=False):
-    """Fused layer vs the oracle for the listed sequences (default all).
-    Returns (number of tie-band selection differences, max-abs where
-    |o| < 0.5, mean-abs)."""
+def layer_parity(w, run=None, seqs=None, tokens=None, strict=False, single=False):
+    """Fused layer (the single-launch one when single) vs the oracle for the
+    listed sequences (default all). Returns (number of tie-band selection
+    differences, max-abs where |o| < 0.5, mean-abs)."""
     run = run or Run(w)
-    res = run.layer()
+    res = run.layer(single=single)
     prm = w.params
     ties, gots, refs = 0, [], []
     for b in (range(prm["num_seqs"]) if seqs is None else seqs):

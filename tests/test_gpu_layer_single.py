@@ -1,0 +1,113 @@
+"""GPU parity of msa_decode_layer_single (one cooperative launch) through the
+C ABI: against the oracle on small ragged batches and on sampled tokens of
+the full-size configurations (tolerances of tests/gpu_util.py), and against
+msa_decode_layer, whose kernels run the same device code: the same selection
+everywhere, and the same output bits where both run the attention with 4
+waves per item (the full-size 128K speculative-verify batch of 32 sequences
+x 4 tokens, and a batch with more (sequence, token, KV head) items than the
+grid has workgroups)."""
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_attention_kv_amd as msa
+from tests import gpu_util as G
+from workloads import make_workload, make_config, KV_NVFP4, KV_BF16, IDX_FP8, IDX_NVFP4, IDX_BF16
+
+pytestmark = pytest.mark.gpu
+
+
+def _same_as_two_kernel(w, run=None):
+    """The selection always matches msa_decode_layer's bit for bit (same
+    pooled scores). The output and lse match bit for bit when the two-kernel
+    attention also runs 4 waves per item, i.e. with at least two items per
+    compute unit; for fewer items it spreads an item over 8 waves, whose
+    partial softmax states merge in another order (the oracle comparison
+    covers those cases)."""
+    run = run or G.Run(w)
+    a = run.layer()
+    b = run.layer(single=True)
+    assert np.array_equal(a["sel"], b["sel"]), (w.name, "selection differs from msa_decode_layer")
+    prm = w.params
+    items = prm["num_seqs"] * prm["q_len"] * prm["num_kv_heads"]
+    if items >= 2 * torch.cuda.get_device_properties(0).multi_processor_count:
+        assert np.array_equal(a["out_bits"], b["out_bits"]), (w.name, "out differs from msa_decode_layer")
+        assert np.array_equal(a["lse"].view(np.uint64), b["lse"].view(np.uint64)), (w.name, "lse differs")
+    else:
+        print("%s: %d items, out max |single - two-kernel| %.2e" % (w.name, items,
+                                                                   np.abs(a["out"] - b["out"]).max()))
+    return run
+
+
+CASES = {
+    # ragged contexts: empty visible range for early tokens (ctx 2 < q_len),
+    # a single partial block, a block boundary, long ones
+    "fp8_q4_ragged": dict(ctx=[2, 100, 129, 3000, 40000, 640], q_len=4, hq=16, hkv=2, hi=8, idx=IDX_FP8),
+    "nvfp4_q4_ragged": dict(ctx=[5, 300, 129, 9000, 257], q_len=4, hq=16, hkv=2, hi=8, idx=IDX_NVFP4),
+    "fp8_q1_hi4": dict(ctx=[7000, 1, 128, 130], q_len=1, hq=8, hkv=1, hi=4, idx=IDX_FP8),
+    "nvfp4_q2_hi4": dict(ctx=[2049, 777], q_len=2, hq=32, hkv=4, hi=4, idx=IDX_NVFP4),
+    "fp8_q3_topk5_nokeep": dict(ctx=[5000, 900, 1300], q_len=3, hq=16, hkv=2, hi=8, idx=IDX_FP8, top_k=5,
+                                keep_last=0),
+}
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_single_matches_oracle_and_two_kernel(name):
+    c = CASES[name]
+    w = make_workload("single_" + name, 61, c["ctx"], c["q_len"], c["hq"], c["hkv"], c["hi"], KV_NVFP4, c["idx"],
+                      table="pool", pool_factor=1.2, n_planted=3, top_k=c.get("top_k", 16),
+                      keep_last=c.get("keep_last", 1))
+    run = _same_as_two_kernel(w)
+    ties, mx, mean = G.layer_parity(w, run=run, single=True)
+    print("%s: ties %d, out max-abs %.2e mean-abs %.2e" % (name, ties, mx, mean))
+
+
+def test_single_more_items_than_grid():
+    # 160 x 4 x 4 = 2560 items: every workgroup loops over several items
+    rng = np.random.default_rng(62)
+    ctx = rng.integers(1, 3000, size=160)
+    w = make_workload("single_many_items", 63, ctx, 4, 16, 4, 8, KV_NVFP4, IDX_FP8, table="permute")
+    run = _same_as_two_kernel(w)
+    ties, mx, mean = G.layer_parity(w, run=run, seqs=[0, 1, 77, 159], single=True)
+    print("many items: ties %d, out max-abs %.2e mean-abs %.2e" % (ties, mx, mean))
+
+
+def test_single_absent_pages():
+    w = make_workload("single_absent", 64, [3000, 1200], 4, 16, 2, 8, KV_NVFP4, IDX_FP8, table="permute")
+    w.block_table[0, 5] = -1
+    w.block_table[1, 3] = w.params["num_pages"] + 2
+    _same_as_two_kernel(w)
+
+
+def test_single_repeat_reuses_workspace():
+    w = make_workload("single_repeat", 65, [4000, 300, 2500], 4, 16, 2, 8, KV_NVFP4, IDX_NVFP4, table="permute")
+    run = G.Run(w)
+    first = run.layer(single=True)
+    for _ in range(3):
+        again = run.layer(single=True)
+        assert np.array_equal(first["out_bits"], again["out_bits"])
+        assert np.array_equal(first["sel"], again["sel"])
+
+
+@pytest.mark.parametrize("cfg,idx", [(2, IDX_FP8), (3, IDX_FP8), (3, IDX_NVFP4), (4, IDX_FP8), (5, IDX_FP8)])
+def test_single_full_size(cfg, idx):
+    # the decode configurations at full size (32K x 8, the 128K speculative
+    # verify batch of 32 x 4 tokens with FP8 and NVFP4 indexer keys, 512K x 4,
+    # 64 ragged sequences); bit for bit against the two-kernel layer, plus the
+    # last sequence's last token against the oracle
+    w = make_config(cfg, idx_dtype=idx)
+    run = _same_as_two_kernel(w)
+    ties, mx, mean = G.layer_parity(w, run=run, seqs=[w.params["num_seqs"] - 1], tokens=[w.params["q_len"] - 1],
+                                    single=True)
+    print("config %d single: ties %d, out max-abs %.2e mean-abs %.2e" % (cfg, ties, mx, mean))
+
+
+def test_single_rejects_unsupported():
+    w = make_workload("single_bf16", 66, [300], 4, 16, 2, 4, KV_BF16, IDX_BF16, table="permute")
+    run = G.Run(w)
+    with pytest.raises(msa.MSAError):
+        run.layer(single=True)
+    w = make_workload("single_q5", 67, [300], 5, 16, 2, 4, KV_NVFP4, IDX_FP8, table="permute")
+    run = G.Run(w)
+    with pytest.raises(msa.MSAError):
+        run.layer(single=True)

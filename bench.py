@@ -2,18 +2,22 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 3]
 
-A step is one call of msa_decode_layer (kernel 1: indexer + per-block max
-pool; kernel 2: top-16 selection + sparse attention) over one batch of the
-chosen synthetic configuration, inputs resident in HBM. Consecutive steps
-rotate over R device replicas of the inputs so that no step finds its bytes
-in the 256 MB Infinity Cache. The K timed steps lie between two HIP events on
-the launch stream. A second pass over the same K steps has every kernel's
+A step is one decode layer over one batch of the chosen synthetic
+configuration, inputs resident in HBM: one call of msa_decode_layer_single
+(one kernel: indexer + per-block max pool, then top-16 selection + sparse
+attention per item) where that path applies and runs the same arithmetic as
+the two-kernel path (--layer auto), else of msa_decode_layer (kernel 1:
+indexer + pool; kernel 2: selection + attention). Consecutive steps rotate
+over R device replicas of the inputs so that no step finds its bytes in the
+256 MB Infinity Cache. The K timed steps lie between two HIP events on the
+launch stream. A second pass over the same K steps has every kernel's
 dispatch record its own start and end events (hipExtLaunchKernel), which
 give the per-kernel durations.
 Prints one JSON line on stdout (details on stderr):
 
   value        decode tokens/s per layer = B * T_q / step time
-  roofline     the dominant kernel (the indexer scan): algorithmic bytes per
+  roofline     the dominant kernel (the single-launch layer kernel, or the
+               indexer scan of the two-kernel path): algorithmic bytes per
                launch / its average duration, against the 8 TB/s HBM peak;
                traffic = HBM bytes per launch from rocprofv3 counters, when a
                record for the current kernel source exists (else null)
@@ -35,10 +39,15 @@ METRIC = "MSA decode tokens/s per layer at 128K ctx; achieved HBM GB/s vs 8 TB/s
 ROOT = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(ROOT, "block_sparse_attention_kv_amd", "csrc")
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "traffic.json")
-# sources that define the indexer kernel's memory traffic
-# the files the indexer kernel's device code is compiled from (the host-side
-# launch helpers it also includes do not change the kernel)
-INDEXER_SOURCES = ("indexer.hip", "fmt.hpp", "indexer_args.hpp")
+# the files each kernel's device code is compiled from (a traffic record is
+# valid only for the sources it was taken on)
+KERNELS = {
+    "indexer_pool": dict(symbol="indexer_pool_kernel",
+                         sources=("indexer.hip", "indexer_impl.hpp", "fmt.hpp", "indexer_args.hpp")),
+    "decode_layer_single": dict(symbol="decode_layer_single_kernel",
+                                sources=("layer.hip", "indexer_impl.hpp", "attn_impl.hpp", "topk.hpp", "fmt.hpp",
+                                         "indexer_args.hpp", "msa_internal.hpp")),
+}
 
 
 def log(*a):
@@ -84,24 +93,32 @@ def attention_bytes(w, sel):
     return int(blocks * G * 128 * per_tok + B * Tq * Hq * 128 * 2 * 2 + B * Tq * prm["top_k"] * 4 + pooled)
 
 
-def traffic_record(config_id):
-    """HBM bytes per indexer launch from the committed counter record, if it
-    was taken on the current indexer source and this workload."""
+def _records():
     try:
-        rec = json.load(open(TRAFFIC_RECORD))
+        recs = json.load(open(TRAFFIC_RECORD))
     except (OSError, ValueError):
-        return None
-    if rec.get("source_sha") != source_sha(INDEXER_SOURCES) or rec.get("config_id") != config_id:
-        return None
-    return rec
+        return []
+    return recs if isinstance(recs, list) else []
 
 
-def write_traffic_record(fetch_csv, write_csv, config_id):
-    """HBM bytes per indexer launch from two rocprofv3 --pmc collections of a
-    --profile-steps run (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch). Each
-    counter is scaled by what it reads for the run's 1 GiB device copy (1 GiB
-    read, 1 GiB written), so the record is in bytes actually moved."""
+def traffic_record(kernel, config_id):
+    """HBM bytes per launch of `kernel` from the committed counter records, if
+    one was taken on the kernel's current sources and this workload."""
+    sha = source_sha(KERNELS[kernel]["sources"])
+    for rec in _records():
+        if rec.get("kernel") == kernel and rec.get("source_sha") == sha and rec.get("config_id") == config_id:
+            return rec
+    return None
+
+
+def write_traffic_record(fetch_csv, write_csv, kernel, config_id):
+    """HBM bytes per launch of `kernel` from two rocprofv3 --pmc collections of
+    a --profile-steps run (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch).
+    Each counter is scaled by what it reads for the run's 1 GiB device copy
+    (1 GiB read, 1 GiB written), so the record is in bytes actually moved.
+    Replaces the record of the same kernel and workload."""
     import csv
+    symbol = KERNELS[kernel]["symbol"]
 
     def per_kernel(path, counter):
         vals, copy = [], None
@@ -109,7 +126,7 @@ def write_traffic_record(fetch_csv, write_csv, config_id):
             if r["Counter_Name"] != counter:
                 continue
             v = float(r["Counter_Value"]) * 1024.0
-            if "indexer_pool_kernel" in r["Kernel_Name"]:
+            if symbol in r["Kernel_Name"]:
                 vals.append(v)
             elif "copyBuffer" in r["Kernel_Name"] and (copy is None or v > copy):
                 copy = v          # the largest copy: the 1 GiB calibration copy
@@ -117,17 +134,21 @@ def write_traffic_record(fetch_csv, write_csv, config_id):
 
     f, fc = per_kernel(fetch_csv, "FETCH_SIZE")
     w, wc = per_kernel(write_csv, "WRITE_SIZE")
+    if not f or not w:
+        raise SystemExit("no %s dispatches in the counter files" % symbol)
     gib = float(1 << 30)
     f_scale, w_scale = gib / fc, gib / wc
     fetch = float(np.mean(f)) * f_scale
     write = float(np.mean(w)) * w_scale
-    rec = {"kernel": "indexer_pool", "config_id": config_id, "source_sha": source_sha(INDEXER_SOURCES),
+    rec = {"kernel": kernel, "config_id": config_id, "source_sha": source_sha(KERNELS[kernel]["sources"]),
            "fetch_bytes_per_launch": fetch, "write_bytes_per_launch": write,
            "traffic_bytes_per_launch": fetch + write, "fetch_scale": f_scale, "write_scale": w_scale,
            "launches": [len(f), len(w)]}
+    recs = [r for r in _records() if not (r.get("kernel") == kernel and r.get("config_id") == config_id)]
+    recs.append(rec)
     os.makedirs(os.path.dirname(TRAFFIC_RECORD), exist_ok=True)
     with open(TRAFFIC_RECORD, "w") as fh:
-        json.dump(rec, fh, indent=1)
+        json.dump(recs, fh, indent=1)
     print(json.dumps(rec))
 
 
@@ -185,13 +206,18 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-steps", type=int, default=0,
                     help="only run this many steps and a 1 GiB calibration copy (for rocprofv3 runs)")
+    ap.add_argument("--layer", choices=("auto", "single", "two"), default="auto",
+                    help="single: msa_decode_layer_single; two: msa_decode_layer; auto: single where it applies "
+                         "and has at least two (sequence, token, KV head) items per compute unit")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
-                    help="write profiles/traffic.json from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE counter "
-                         "collections of a --profile-steps run, and exit")
+                    help="write a record of profiles/traffic.json from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE "
+                         "counter collections of a --profile-steps run, and exit")
+    ap.add_argument("--traffic-kernel", choices=sorted(KERNELS), default="decode_layer_single",
+                    help="the kernel whose counters --traffic-from records")
     args = ap.parse_args()
     wkey = str(args.config) if args.idx_dtype == "fp8" else "%d/%s" % (args.config, args.idx_dtype)
     if args.traffic_from:
-        write_traffic_record(args.traffic_from[0], args.traffic_from[1], wkey)
+        write_traffic_record(args.traffic_from[0], args.traffic_from[1], args.traffic_kernel, wkey)
         return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (one GPU's share of the decode "
@@ -237,13 +263,28 @@ def main():
         call_args.append([ctypes.byref(params), ctypes.byref(c), vp(qs["q"]), vp(qs["idx_q"]), vp(qs["idx_w"]),
                           vp(out), vp(lse), vp(sel), vp(ws), ctypes.c_size_t(ws_bytes), stream])
 
+    items = B * Tq * prm["num_kv_heads"]
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    single_ok = prm["kv_dtype"] == 1 and prm["idx_dtype"] in (1, 2) and Tq <= 4
+    if args.layer == "auto":
+        single = single_ok and items >= 2 * cus
+    else:
+        single = args.layer == "single"
+        if single and not single_ok:
+            raise SystemExit("--layer single: this configuration needs the two-kernel path")
+    kernel = "decode_layer_single" if single else "indexer_pool"
+    plain = L.msa_decode_layer_single if single else L.msa_decode_layer
+    traced = L.msa_decode_layer_single_traced if single else L.msa_decode_layer_traced
+    entry = "msa_decode_layer_single" if single else "msa_decode_layer"
+    log("layer path: %s (%d items, %d compute units)" % (entry, items, cus))
+
     def step(i, events=None):
         if events is None:
-            st = L.msa_decode_layer(*call_args[i % R])
+            st = plain(*call_args[i % R])
         else:
-            st = L.msa_decode_layer_traced(*call_args[i % R], events)
+            st = traced(*call_args[i % R], events)
         if st != 0:
-            raise RuntimeError("msa_decode_layer: %s" % L.msa_last_error().decode())
+            raise RuntimeError("%s: %s" % (entry, L.msa_last_error().decode()))
 
     if args.profile_steps:
         for i in range(args.profile_steps):
@@ -282,7 +323,8 @@ def main():
     # recording its own start and end event (hipExtLaunchKernel); the events
     # lengthen the step a little, so the step time above comes from the
     # uninstrumented pass
-    n_st = msa.NUM_STAGES
+    n_st = 1 if single else msa.NUM_STAGES
+    stage_names = ["decode_layer_single"] if single else list(msa.STAGE_NAMES)
     kev = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * n_st)] for _ in range(args.steps)]
     for row in kev:          # create the HIP events before the timed pass
         for e in row:
@@ -298,7 +340,7 @@ def main():
     ms_step_traced = k0.elapsed_time(k1) / args.steps
     stage_ms = [float(np.mean([kev[i][2 * s].elapsed_time(kev[i][2 * s + 1]) for i in range(args.steps)]))
                 for s in range(n_st)]
-    log("kernels (ms): " + ", ".join("%s %.4f" % (n, v) for n, v in zip(msa.STAGE_NAMES, stage_ms)) +
+    log("kernels (ms): " + ", ".join("%s %.4f" % (n, v) for n, v in zip(stage_names, stage_ms)) +
         "; step with kernel events %.4f ms" % ms_step_traced)
 
     # ---- attainable copy bandwidth on this machine (context)
@@ -318,10 +360,15 @@ def main():
     idx_b = indexer_bytes(w)
     att_b = attention_bytes(w, gpu_res["sel"])
     step_b = idx_b + att_b
-    idx_gbps = idx_b / (stage_ms[0] * 1e-3) / 1e9
-    att_gbps = att_b / (stage_ms[1] * 1e-3) / 1e9
     step_gbps = step_b / (ms_step * 1e-3) / 1e9
-    rec = traffic_record(wkey)
+    if single:   # one kernel moves the step's bytes
+        kern_b, kern_ms = step_b, stage_ms[0]
+        stage_detail = {}
+    else:        # the indexer kernel dominates
+        kern_b, kern_ms = idx_b, stage_ms[0]
+        stage_detail = {"attention_gbps": att_b / (stage_ms[1] * 1e-3) / 1e9}
+    kern_gbps = kern_b / (kern_ms * 1e-3) / 1e9
+    rec = traffic_record(kernel, wkey)
     tokens = B * Tq
     res = {
         "metric": METRIC,
@@ -342,14 +389,14 @@ def main():
                    "ctx_len": int(w.ctx_lens.max()), "q_heads": Hq, "kv_heads": prm["num_kv_heads"],
                    "idx_heads": prm["idx_heads"], "top_k": prm["top_k"], "block": 128,
                    "input_replicas": R},
-        "roofline": {"bound": "hbm", "kernel": "indexer_pool", "achieved": idx_gbps, "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": idx_gbps / HBM_PEAK_GBPS,
+        "roofline": {"bound": "hbm", "kernel": kernel, "achieved": kern_gbps, "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": kern_gbps / HBM_PEAK_GBPS,
                      "traffic": None if rec is None else rec["traffic_bytes_per_launch"],
-                     "algorithmic_bytes": idx_b, "avg_ms": stage_ms[0]},
-        "step": {"algorithmic_bytes": step_b, "gbps": step_gbps, "frac": step_gbps / HBM_PEAK_GBPS,
-                 "stage_ms": dict(zip(msa.STAGE_NAMES, stage_ms)), "ms_per_step_with_kernel_events": ms_step_traced,
-                 "attention_bytes": att_b,
-                 "attention_gbps": att_gbps, "copy_gbps_attainable": copy_gbps},
+                     "algorithmic_bytes": kern_b, "avg_ms": kern_ms},
+        "step": dict({"entry": entry, "algorithmic_bytes": step_b, "gbps": step_gbps,
+                      "frac": step_gbps / HBM_PEAK_GBPS, "stage_ms": dict(zip(stage_names, stage_ms)),
+                      "ms_per_step_with_kernel_events": ms_step_traced, "indexer_bytes": idx_b,
+                      "attention_bytes": att_b, "copy_gbps_attainable": copy_gbps}, **stage_detail),
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, gpu_res, args.cpu_budget)

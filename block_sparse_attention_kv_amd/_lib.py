@@ -79,6 +79,7 @@ def load():
         "msa_decode_layer": (st, [P, C, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
         "msa_decode_layer_traced": (st, [P, C, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp]),
         "msa_decode_layer_single": (st, [P, C, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+        "msa_decode_layer_single_traced": (st, [P, C, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp]),
         "msa_kv_insert": (st, [P, C, vp, vp, vp, vp]),
         "msa_debug_dequant_nvfp4": (st, [vp, vp, i64, vp, vp]),
         "msa_debug_dequant_fp8": (st, [vp, i64, vp, vp]),
@@ -95,7 +96,8 @@ def load():
 
 
 EXPORTED = ("msa_workspace_size", "msa_indexer_scores", "msa_pool_select_blocks", "msa_sparse_attn_decode",
-            "msa_decode_layer", "msa_decode_layer_traced", "msa_decode_layer_single", "msa_kv_insert", "msa_debug_dequant_nvfp4",
+            "msa_decode_layer", "msa_decode_layer_traced", "msa_decode_layer_single",
+            "msa_decode_layer_single_traced", "msa_kv_insert", "msa_debug_dequant_nvfp4",
             "msa_debug_dequant_fp8",
             "msa_status_string", "msa_last_error", "msa_version")
 

@@ -347,9 +347,10 @@ msa_status_t msa_decode_layer(const msa_params_t* p, const msa_cache_t* c, const
   return msa_decode_layer_traced(p, c, q, idx_q, idx_w, out, lse, sel_out, workspace, ws_bytes, stream, nullptr);
 }
 
-msa_status_t msa_decode_layer_single(const msa_params_t* p, const msa_cache_t* c, const void* q, const void* idx_q,
-                                     const float* idx_w, void* out, float* lse, int32_t* sel_out, void* workspace,
-                                     size_t ws_bytes, void* stream) {
+msa_status_t msa_decode_layer_single_traced(const msa_params_t* p, const msa_cache_t* c, const void* q,
+                                            const void* idx_q, const float* idx_w, void* out, float* lse,
+                                            int32_t* sel_out, void* workspace, size_t ws_bytes, void* stream,
+                                            void* const* ev) {
   g_err[0] = 0;
   msa_status_t st = check_params(p);
   if (st != MSA_OK) return st;
@@ -370,9 +371,17 @@ msa_status_t msa_decode_layer_single(const msa_params_t* p, const msa_cache_t* c
   ia.pooled = pooled;
   AttnArgs aa = attn_args(p, c, q, pooled, sel_out, out, lse);
   set_splits(aa, p, nullptr, 0);  // one workgroup per item
+  const KTimer tm = stage_timer(ev, 0);
   hipError_t e = launch_layer_single(ia, aa, reinterpret_cast<uint32_t*>(ws + L.done_off), next_epoch(),
-                                     p->idx_dtype, p->idx_heads <= 4 ? 4 : 8, static_cast<hipStream_t>(stream));
+                                     p->idx_dtype, p->idx_heads <= 4 ? 4 : 8, static_cast<hipStream_t>(stream), &tm);
   return e == hipSuccess ? MSA_OK : hip_fail(e, "single-launch layer");
+}
+
+msa_status_t msa_decode_layer_single(const msa_params_t* p, const msa_cache_t* c, const void* q, const void* idx_q,
+                                     const float* idx_w, void* out, float* lse, int32_t* sel_out, void* workspace,
+                                     size_t ws_bytes, void* stream) {
+  return msa_decode_layer_single_traced(p, c, q, idx_q, idx_w, out, lse, sel_out, workspace, ws_bytes, stream,
+                                        nullptr);
 }
 
 msa_status_t msa_kv_insert(const msa_params_t* p, const msa_cache_t* c, const void* new_k, const void* new_v,

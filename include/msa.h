@@ -254,6 +254,15 @@ msa_status_t msa_decode_layer_single(const msa_params_t* p, const msa_cache_t* c
                                      void* out, float* lse, int32_t* sel_out,
                                      void* workspace, size_t ws_bytes, void* stream);
 
+/* msa_decode_layer_single with a tracing hook: when `events` is not NULL it
+ * holds 2 hipEvent_t handles (NULL entries allowed) into which the kernel's
+ * dispatch records its start and end (hipExtLaunchKernel). */
+msa_status_t msa_decode_layer_single_traced(const msa_params_t* p, const msa_cache_t* cache,
+                                            const void* q, const void* idx_q, const float* idx_w,
+                                            void* out, float* lse, int32_t* sel_out,
+                                            void* workspace, size_t ws_bytes, void* stream,
+                                            void* const* events);
+
 /* KV-insert: quantise the q_len new tokens of every sequence and write them
  * into the paged caches -- the step that precedes the decode of those tokens
  * [ainewsbites page "vLLM Adds Day-0 Support for MiniMax-M3.1-Flash on NVIDIA

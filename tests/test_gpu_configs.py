@@ -1,6 +1,8 @@
 """GPU parity at the full sizes of the large decode configurations, in the
-launch configuration bench.py times: the whole batch runs through
-msa_decode_layer, and the oracle recomputes sampled sequences one by one
+launch configurations bench.py times: the whole batch runs through
+msa_decode_layer (every configuration) or msa_decode_layer_single (the 128K
+speculative-verify batch, where bench.py's automatic choice takes the
+single-launch path), and the oracle recomputes sampled sequences one by one
 (selection tie-aware, outputs to the strict max-abs 2e-3 / mean-abs 2e-4)."""
 import numpy as np
 import pytest
@@ -11,11 +13,12 @@ from workloads import make_config
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("cfg,seqs", [(3, [0, 21]), (4, [0, 3])])
-def test_config_full_size_sampled(cfg, seqs):
+@pytest.mark.parametrize("cfg,seqs,single", [(3, [0, 21], False), (3, [10, 31], True), (4, [0, 3], False)])
+def test_config_full_size_sampled(cfg, seqs, single):
     w = make_config(cfg)
-    ties, mx, mean = G.layer_parity(w, seqs=seqs, strict=True)
-    print("cfg%d sampled %s: tie-band selections %d, out max-abs %.2e mean-abs %.2e" % (cfg, seqs, ties, mx, mean))
+    ties, mx, mean = G.layer_parity(w, seqs=seqs, strict=True, single=single)
+    print("cfg%d%s sampled %s: tie-band selections %d, out max-abs %.2e mean-abs %.2e" % (
+        cfg, " single-launch" if single else "", seqs, ties, mx, mean))
 
 
 def test_config5_ragged_sampled():
@@ -27,11 +30,11 @@ def test_config5_ragged_sampled():
         seqs, [int(w.ctx_lens[s]) for s in seqs], ties, mx, mean))
 
 
-@pytest.mark.parametrize("cfg,seqs", [(3, [5]), (4, [1])])
-def test_config_full_size_nvfp4_index_keys_sampled(cfg, seqs):
+@pytest.mark.parametrize("cfg,seqs,single", [(3, [5], True), (4, [1], False)])
+def test_config_full_size_nvfp4_index_keys_sampled(cfg, seqs, single):
     # the same workloads with NVFP4 indexer keys (bench.py --idx-dtype nvfp4)
     from workloads import IDX_NVFP4
     w = make_config(cfg, idx_dtype=IDX_NVFP4)
-    ties, mx, mean = G.layer_parity(w, seqs=seqs, strict=True)
+    ties, mx, mean = G.layer_parity(w, seqs=seqs, strict=True, single=single)
     print("cfg%d nvfp4 keys sampled %s: tie-band selections %d, out max-abs %.2e mean-abs %.2e" % (
         cfg, seqs, ties, mx, mean))

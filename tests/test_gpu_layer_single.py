@@ -111,3 +111,32 @@ def test_single_rejects_unsupported():
     run = G.Run(w)
     with pytest.raises(msa.MSAError):
         run.layer(single=True)
+
+
+def test_single_traced_matches_plain():
+    # the traced entry records the kernel's start and end into two events and
+    # computes the same result
+    import ctypes
+    w = make_workload("single_traced", 68, [3000, 700], 4, 16, 2, 8, KV_NVFP4, IDX_FP8, table="permute")
+    run = G.Run(w)
+    want = run.layer(single=True)
+    prm = w.params
+    B, Tq, Hq, K = prm["num_seqs"], prm["q_len"], prm["num_q_heads"], prm["top_k"]
+    out = torch.empty((B, Tq, Hq, 128), dtype=torch.int16, device="cuda")
+    sel = torch.empty((B, Tq, K), dtype=torch.int32, device="cuda")
+    ws = msa.alloc_workspace(run.params, "cuda")
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    for e in ev:
+        e.record()
+    arr = (ctypes.c_void_p * 2)(*[e.cuda_event for e in ev])
+    c = run.cache.c()
+    vp = lambda t: ctypes.c_void_p(t.data_ptr())
+    st = msa.load().msa_decode_layer_single_traced(
+        ctypes.byref(run.params), ctypes.byref(c), vp(run.q), vp(run.idx_q), vp(run.idx_w), vp(out), None, vp(sel),
+        vp(ws), ctypes.c_size_t(ws.numel() * ws.element_size()),
+        ctypes.c_void_p(torch.cuda.current_stream().cuda_stream), arr)
+    assert st == 0
+    torch.cuda.synchronize()
+    assert ev[0].elapsed_time(ev[1]) > 0
+    assert np.array_equal(out.cpu().numpy(), want["out_bits"])
+    assert np.array_equal(sel.cpu().numpy(), want["sel"])

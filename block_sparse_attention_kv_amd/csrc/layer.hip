@@ -80,6 +80,10 @@ __global__ __launch_bounds__(64 * kLayerWaves, kLayerWgsPerCu) void decode_layer
   const AttnArgs& aa = L.aa;
   const int item = blockIdx.x - L.idx_wgs;
   const int b = item / aa.Hkv / aa.Tq;
+  // The later half of the items is dispatched last and ends the kernel; its
+  // waves share compute units with older attention waves of the first half,
+  // which win issue arbitration by age. Raise their priority instead.
+  if (2 * item >= aa.B * aa.Tq * aa.Hkv) __builtin_amdgcn_s_setprio(1);
 
   // work blocks before sequence b and in total (the indexer's numbering)
   int64_t before = 0, total = 0;

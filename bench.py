@@ -196,8 +196,8 @@ def cpu_baseline(w, gpu_res, budget_s=20.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--config", type=int, default=3)
     ap.add_argument("--idx-dtype", choices=("fp8", "nvfp4"), default="fp8",
                     help="indexer-key format (the measured configurations use fp8)")

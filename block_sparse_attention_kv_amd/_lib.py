@@ -83,6 +83,7 @@ def load():
         "msa_kv_insert": (st, [P, C, vp, vp, vp, vp]),
         "msa_debug_dequant_nvfp4": (st, [vp, vp, i64, vp, vp]),
         "msa_debug_dequant_fp8": (st, [vp, i64, vp, vp]),
+        "msa_debug_layer_spin_limit": (st, [ctypes.c_int32]),
         "msa_status_string": (ctypes.c_char_p, [st]),
         "msa_last_error": (ctypes.c_char_p, []),
         "msa_version": (ctypes.c_char_p, []),
@@ -98,7 +99,7 @@ def load():
 EXPORTED = ("msa_workspace_size", "msa_indexer_scores", "msa_pool_select_blocks", "msa_sparse_attn_decode",
             "msa_decode_layer", "msa_decode_layer_traced", "msa_decode_layer_single",
             "msa_decode_layer_single_traced", "msa_kv_insert", "msa_debug_dequant_nvfp4",
-            "msa_debug_dequant_fp8",
+            "msa_debug_dequant_fp8", "msa_debug_layer_spin_limit",
             "msa_status_string", "msa_last_error", "msa_version")
 
 
@@ -244,6 +245,12 @@ def msa_debug_dequant_nvfp4(codes, scales, out, stream=None):
     n_groups = scales.numel()
     _check(load().msa_debug_dequant_nvfp4(_ptr(codes), _ptr(scales), n_groups, _ptr(out), _stream(stream)),
            "msa_debug_dequant_nvfp4")
+
+
+def msa_debug_layer_spin_limit(polls):
+    """Poll limit of msa_decode_layer_single's waits for later calls (0 =
+    default)."""
+    _check(load().msa_debug_layer_spin_limit(int(polls)), "msa_debug_layer_spin_limit")
 
 
 def msa_debug_dequant_fp8(codes, out, stream=None):

@@ -20,8 +20,9 @@
 // workgroups wait on nothing, so the waits end; as indexer workgroups retire,
 // attention workgroups take their slots. One flag per workgroup, written by
 // one thread: no contended atomics, and no clearing (a flag of an older call
-// holds another epoch). A wait is also bounded (about a second): a workgroup
-// that gives up writes NaN outputs.
+// holds another epoch). A wait is also bounded (about a second; a debug
+// export can lower the bound): a workgroup that gives up writes NaN outputs
+// and lse and a selection of -1.
 //
 // Coherence. The compute units of different XCDs have separate L2 caches, so
 // a device-scope release / acquire fence writes back / invalidates the L2;
@@ -37,6 +38,8 @@
 // bit, and so does the output wherever that path's attention also runs 4
 // waves per item (batches with at least two items per compute unit).
 // Supported: NVFP4 K/V, FP8 or NVFP4 indexer keys, q_len <= 4.
+#include <atomic>
+
 #include "indexer_impl.hpp"
 #include "attn_impl.hpp"
 
@@ -48,12 +51,16 @@ constexpr int kLayerWaves = 4;
 constexpr int kLayerWgsPerCu = 2;
 constexpr int kSpinLimit = 1 << 22;  // polls of one flag (~100 ns each)
 
+// Poll limit of the next launches (0: kSpinLimit); set by a debug export.
+std::atomic<int> g_spin_limit{0};
+
 struct LayerArgs {
   IndexerArgs ia;
   AttnArgs aa;
   uint32_t* wg_done;    // [idx_wgs]: epoch once the workgroup's ranges are pooled
   uint32_t epoch;
   int idx_wgs;          // workgroups running the indexer
+  int spin_limit;       // polls of one flag before an item gives up
 };
 
 // Indexer wave covering global work block g (the inverse of the split
@@ -113,17 +120,18 @@ __global__ __launch_bounds__(64 * kLayerWaves, kLayerWgsPerCu) void decode_layer
     for (int64_t w = wg_lo + tid; w <= wg_hi; w += 64 * kLayerWaves) {
       int n = 0;
       while (__hip_atomic_load(L.wg_done + w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != L.epoch &&
-             ++n < kSpinLimit)
+             ++n < L.spin_limit)
         __builtin_amdgcn_s_sleep(2);
-      if (n >= kSpinLimit) gave_up = 1;
+      if (n >= L.spin_limit) gave_up = 1;
     }
   }
   __syncthreads();
-  if (gave_up) {  // mark this item's results invalid
+  if (gave_up) {  // mark this item's results invalid: NaN output and lse, no selection
     const int bt = item / aa.Hkv, g = item % aa.Hkv;
     uint16_t* orow = aa.out + ((size_t)bt * aa.Hq + (size_t)g * aa.grp) * kHeadDim;
     for (int i = tid; i < aa.grp * kHeadDim; i += 64 * kLayerWaves) orow[i] = 0x7FC0;
     if (aa.lse && tid < aa.grp) aa.lse[(size_t)bt * aa.Hq + g * aa.grp + tid] = __builtin_nanf("");
+    if (g == 0 && aa.sel && tid < aa.top_k) aa.sel[(size_t)bt * aa.top_k + tid] = -1;
     return;
   }
   attn_body<true, kLayerWaves, true>(aa, item, lds, tid);
@@ -147,6 +155,8 @@ hipError_t launch_single_hp(const LayerArgs& L, int items, hipStream_t s, const 
 
 }  // namespace
 
+void set_layer_spin_limit(int polls) { g_spin_limit.store(polls, std::memory_order_relaxed); }
+
 hipError_t launch_layer_single(const IndexerArgs& ia, const AttnArgs& aa, uint32_t* wg_done, uint32_t epoch,
                                int key_format, int hp, hipStream_t s, const KTimer* tm) {
   if (!ia.pooled || ia.scores || aa.pooled != ia.pooled || aa.splits != 1 || !wg_done) return hipErrorInvalidValue;
@@ -158,7 +168,8 @@ hipError_t launch_layer_single(const IndexerArgs& ia, const AttnArgs& aa, uint32
   const int64_t need = ((int64_t)ia.B * ia.maxb + 3) / 4;  // at least one block per wave
   if (n_idx > need) n_idx = need;
   if (items < 1 || n_idx + items > INT32_MAX || n_idx > kLayerMaxIdxWgs) return hipErrorInvalidValue;
-  LayerArgs L{ia, aa, wg_done, epoch, (int)n_idx};
+  const int limit = g_spin_limit.load(std::memory_order_relaxed);
+  LayerArgs L{ia, aa, wg_done, epoch, (int)n_idx, limit > 0 ? limit : kSpinLimit};
   switch (key_format) {
     case kKfFp8:
       return hp == 8 ? launch_single_hp<kKfFp8, 8>(L, (int)items, s, tm) : launch_single_hp<kKfFp8, 4>(L, (int)items, s, tm);

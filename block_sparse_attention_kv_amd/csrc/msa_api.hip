@@ -437,6 +437,13 @@ msa_status_t msa_kv_insert(const msa_params_t* p, const msa_cache_t* c, const vo
   return e == hipSuccess ? MSA_OK : hip_fail(e, "insert launch");
 }
 
+msa_status_t msa_debug_layer_spin_limit(int32_t polls) {
+  g_err[0] = 0;
+  if (polls < 0) return fail(MSA_ERR_INVALID_ARG, "polls must be >= 0");
+  set_layer_spin_limit(polls);
+  return MSA_OK;
+}
+
 msa_status_t msa_debug_dequant_nvfp4(const uint8_t* codes, const uint8_t* scales, int64_t n_groups, float* out,
                                      void* stream) {
   g_err[0] = 0;

@@ -107,6 +107,9 @@ hipError_t launch_attn(const AttnArgs& a, bool nvfp4, int waves, hipStream_t s, 
 constexpr int kLayerMaxIdxWgs = 4096;
 hipError_t launch_layer_single(const IndexerArgs& ia, const AttnArgs& aa, uint32_t* wg_done, uint32_t epoch,
                                int key_format, int hp, hipStream_t s, const KTimer* t = nullptr);
+// Poll limit of the single-launch layer's waits for later launches (0: the
+// default of about a second).
+void set_layer_spin_limit(int polls);
 hipError_t launch_debug_nvfp4(const uint8_t* codes, const uint8_t* scales, int64_t n_groups,
                               float* out, hipStream_t s);
 hipError_t launch_debug_fp8(const uint8_t* codes, int64_t n, float* out, hipStream_t s);

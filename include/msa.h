@@ -306,6 +306,15 @@ msa_status_t msa_debug_dequant_nvfp4(const uint8_t* codes, const uint8_t* scales
 msa_status_t msa_debug_dequant_fp8(const uint8_t* codes, int64_t n, float* out,
                                    void* stream);
 
+/* Debug export: the number of polls after which a workgroup of
+ * msa_decode_layer_single stops waiting for the indexer workgroups that
+ * cover its sequence (default, polls = 0: about a second of polling). An
+ * item that stops writes NaN to its out rows and lse entries and -1 to its
+ * selection; the kernel still ends normally. Applies to later calls in this
+ * process; polls < 0 returns MSA_ERR_INVALID_ARG. For tests of the bounded
+ * wait. */
+msa_status_t msa_debug_layer_spin_limit(int32_t polls);
+
 /* Human-readable name of a status code (static string). */
 const char* msa_status_string(msa_status_t s);
 /* Thread-local description of the last failure in this thread ("" if none). */

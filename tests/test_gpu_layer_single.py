@@ -140,3 +140,47 @@ def test_single_traced_matches_plain():
     assert ev[0].elapsed_time(ev[1]) > 0
     assert np.array_equal(out.cpu().numpy(), want["out_bits"])
     assert np.array_equal(sel.cpu().numpy(), want["sel"])
+
+
+def test_single_bounded_wait_gives_up_cleanly():
+    # With a poll limit of 1 an attention workgroup that finds its indexer
+    # workgroups unfinished at the first poll gives up at once: the kernel
+    # still ends, every item is either the normal result or marked invalid
+    # (NaN output and lse, selection -1), and the default limit restores the
+    # normal result on the next call.
+    w = make_workload("single_spin", 69, [20000] * 24, 4, 16, 2, 8, KV_NVFP4, IDX_FP8, table="permute")
+    run = G.Run(w)
+    want = run.layer(single=True)
+    try:
+        msa.msa_debug_layer_spin_limit(1)
+        got = run.layer(single=True)
+    finally:
+        msa.msa_debug_layer_spin_limit(0)
+    prm = w.params
+    B, Tq, Hkv, grp = prm["num_seqs"], prm["q_len"], prm["num_kv_heads"], prm["num_q_heads"] // prm["num_kv_heads"]
+    gave_up = 0
+    for b in range(B):
+        for t in range(Tq):
+            for g in range(Hkv):
+                heads = slice(g * grp, (g + 1) * grp)
+                o = got["out_bits"][b, t, heads]
+                if np.all(o.view(np.uint16) == 0x7FC0):
+                    assert np.all(np.isnan(got["lse"][b, t, heads]))
+                    if g == 0:
+                        assert np.all(got["sel"][b, t] == -1)
+                    gave_up += 1
+                else:
+                    assert np.array_equal(o, want["out_bits"][b, t, heads]), (b, t, g)
+                    if g == 0:
+                        assert np.array_equal(got["sel"][b, t], want["sel"][b, t]), (b, t)
+                    assert np.array_equal(got["lse"][b, t, heads].view(np.uint64),
+                                          want["lse"][b, t, heads].view(np.uint64)), (b, t, g)
+    print("items that gave up with a poll limit of 1: %d of %d" % (gave_up, B * Tq * Hkv))
+    again = run.layer(single=True)
+    assert np.array_equal(again["out_bits"], want["out_bits"])
+    assert np.array_equal(again["sel"], want["sel"])
+
+
+def test_single_spin_limit_rejects_negative():
+    with pytest.raises(msa.MSAError):
+        msa.msa_debug_layer_spin_limit(-1)

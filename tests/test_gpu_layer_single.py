@@ -184,3 +184,31 @@ def test_single_bounded_wait_gives_up_cleanly():
 def test_single_spin_limit_rejects_negative():
     with pytest.raises(msa.MSAError):
         msa.msa_debug_layer_spin_limit(-1)
+
+
+def test_single_edge_contexts():
+    # an empty sequence, 1 token, partial blocks, exactly 16 blocks, 16 blocks
+    # + 1 token, ctx < q_len, and a context longer than the block table
+    # (clamped to max_blocks * 128)
+    w = make_workload("single_edges", 71, [0, 1, 127, 128, 129, 2047, 2048, 2049, 2176, 2, 3000], 2, 16, 2, 8,
+                      KV_NVFP4, IDX_FP8, table="permute")
+    w.ctx_lens[-1] = w.params["max_blocks_per_seq"] * 128 + 700
+    run = _same_as_two_kernel(w)
+    ties, mx, mean = G.layer_parity(w, run=run, single=True)
+    print("edges: ties %d, out max-abs %.2e mean-abs %.2e" % (ties, mx, mean))
+
+
+@pytest.mark.parametrize("k_ts,v_ts,sm", [(0.75, 1.5, 0.05), (-0.5, 1.0, 0.0)])
+def test_single_tensor_and_softmax_scales(k_ts, v_ts, sm):
+    w = make_workload("single_scales", 72, [1000, 4000, 300], 2, 16, 2, 8, KV_NVFP4, IDX_NVFP4, table="permute",
+                      k_tensor_scale=k_ts, v_tensor_scale=v_ts, softmax_scale=sm)
+    run = _same_as_two_kernel(w)
+    G.layer_parity(w, run=run, single=True)
+
+
+@pytest.mark.parametrize("k,keep", [(4, 1), (16, 0), (1, 1)])
+def test_single_top_k_and_keep_last(k, keep):
+    w = make_workload("single_k%d_keep%d" % (k, keep), 73, [3000, 700], 1, 8, 1, 4, KV_NVFP4, IDX_FP8,
+                      table="permute", top_k=k, keep_last=keep, n_planted=2)
+    run = _same_as_two_kernel(w)
+    G.layer_parity(w, run=run, single=True)

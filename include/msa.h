@@ -27,7 +27,9 @@
  * ------------------------------------------------------------------------
  * Ownership.  Every buffer is allocated and freed by the caller. The library
  *   keeps no pointer after a call returns and never allocates device memory;
- *   scratch memory comes only from the caller's workspace argument.
+ *   scratch memory comes only from the caller's workspace argument. A
+ *   workspace belongs to one call at a time: calls that may run at the same
+ *   time (on different streams) need workspaces of their own.
  * Pointers.  Pointers named "device" must point to device memory of the
  *   current HIP device. msa_params_t and msa_cache_t themselves are host
  *   structures read during the call only.

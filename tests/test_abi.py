@@ -166,3 +166,35 @@ def test_binding_raises_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="not built"):
         _lib.load()
+
+
+def test_single_launch_layer_args_rejected():
+    # msa_decode_layer_single: unsupported problems, null pointers and a short
+    # workspace are reported before anything is launched
+    L = msa.load()
+    fake = ctypes.c_void_p(0x1000)
+    nv = msa.Cache(fake, fake, fake, fake, 1.0, 1.0, fake, fake, fake, fake, 1.0)
+    bf = msa.Cache(fake, None, fake, None, 1.0, 1.0, fake, None, fake, fake)
+    for over, cache in ((dict(kv_dtype=0, idx_dtype=0), bf),        # bf16 K/V
+                        (dict(kv_dtype=1, idx_dtype=0), nv),        # bf16 indexer keys
+                        (dict(kv_dtype=1, idx_dtype=1, q_len=5, idx_heads=4), nv)):  # q_len > 4
+        p = _params(**over)
+        st, msg = _status(L.msa_decode_layer_single, ctypes.byref(p), ctypes.byref(cache), fake, fake, fake, fake,
+                          None, None, fake, 1 << 30, None)
+        assert st == _lib.MSA_ERR_UNSUPPORTED, (over, st, msg)
+    p = _params(kv_dtype=1, idx_dtype=1)
+    need = msa.msa_workspace_size(p)
+    assert L.msa_decode_layer_single(ctypes.byref(p), ctypes.byref(nv), None, fake, fake, fake, None, None, fake,
+                                     need, None) == _lib.MSA_ERR_INVALID_ARG
+    assert L.msa_decode_layer_single(ctypes.byref(p), ctypes.byref(nv), fake, fake, fake, fake, None, None, fake,
+                                     need - 1, None) == _lib.MSA_ERR_WORKSPACE
+    assert L.msa_decode_layer_single(ctypes.byref(p), ctypes.byref(nv), fake, fake, fake, fake, None, None,
+                                     ctypes.c_void_p(0x1010), need, None) == _lib.MSA_ERR_WORKSPACE
+    assert L.msa_decode_layer_single(None, ctypes.byref(nv), fake, fake, fake, fake, None, None, fake, need,
+                                     None) == _lib.MSA_ERR_INVALID_ARG
+
+
+def test_debug_spin_limit_argument():
+    L = msa.load()
+    assert L.msa_debug_layer_spin_limit(-5) == _lib.MSA_ERR_INVALID_ARG
+    assert L.msa_debug_layer_spin_limit(0) == _lib.MSA_OK

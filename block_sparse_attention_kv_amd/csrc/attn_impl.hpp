@@ -229,6 +229,10 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, int wg, uint8_t* ld
   }
   __syncthreads();
   const int n = __builtin_amdgcn_readfirstlane(nlist);
+  if constexpr (COHERENT) {  // single launch: the selection ran at priority 3 (see layer.hip)
+    if (2 * item >= a.B * a.Tq * a.Hkv) __builtin_amdgcn_s_setprio(1);
+    else __builtin_amdgcn_s_setprio(0);
+  }
 
   SoftmaxState st;
   st.m = -INFINITY;

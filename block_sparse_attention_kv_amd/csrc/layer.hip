@@ -87,10 +87,15 @@ __global__ __launch_bounds__(64 * kLayerWaves, kLayerWgsPerCu) void decode_layer
   const AttnArgs& aa = L.aa;
   const int item = blockIdx.x - L.idx_wgs;
   const int b = item / aa.Hkv / aa.Tq;
-  // The later half of the items is dispatched last and ends the kernel; its
-  // waves share compute units with older attention waves of the first half,
-  // which win issue arbitration by age. Raise their priority instead.
-  if (2 * item >= aa.B * aa.Tq * aa.Hkv) __builtin_amdgcn_s_setprio(1);
+  // Until its selection is made an item runs at the highest wave priority:
+  // the flag wait and the selection are a chain of dependent steps with
+  // little issue work, on the critical path of every item, while the waves
+  // it shares a compute unit with stream keys. attn_body drops the priority
+  // once the blocks are known (to 1 for the later half of the items, which
+  // is dispatched last and ends the kernel: its waves share compute units
+  // with older attention waves of the first half, which win issue
+  // arbitration by age; to 0 for the rest).
+  __builtin_amdgcn_s_setprio(3);
 
   // work blocks before sequence b and in total (the indexer's numbering)
   int64_t before = 0, total = 0;

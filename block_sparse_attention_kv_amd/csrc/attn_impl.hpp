@@ -108,9 +108,12 @@ __device__ __forceinline__ void load_v(const KvRsrc& r, const LaneOff& o, VRegs&
 // W waves; lds: the dynamic LDS region (attn_lds_bytes); tid: threadIdx.x
 // (a caller that loops over items passes it through an empty asm statement,
 // so that the lane-dependent set-up is redone per item instead of being
-// hoisted and held in registers across the loop). COHERENT: read the pooled
-// scores with device-scope relaxed atomic loads (written by the same grid).
-// Every thread of the workgroup calls it.
+// hoisted and held in registers across the loop). COHERENT: the pooled
+// scores are tagged 64-bit words written by the same grid (indexer_body),
+// read with device-scope atomic loads until they carry a.epoch, a.spin_limit
+// polls at most; an item that gives up writes NaN to its out rows and lse
+// entries and -1 to its selection instead of attending. Every thread of the
+// workgroup calls it.
 template <bool NVFP4, int W, bool COHERENT = false>
 __device__ __forceinline__ void attn_body(const AttnArgs& a, int wg, uint8_t* lds, int tid) {
   typedef MfmaT<NVFP4> MT;
@@ -151,13 +154,25 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, int wg, uint8_t* ld
   if (a.pooled) {
     const int nvis = p < 0 ? 0 : p / kBlock + 1;
     const float* src = a.pooled + (size_t)bt * a.maxb;
-    nsel = block_topk<NT>(
-        [&](int i) {
-          if constexpr (COHERENT) return __hip_atomic_load(src + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          else return src[i];
-        },
-        [&](int i) { return bt_row[i]; }, pages, nvis,
-                          a.top_k, a.keep_last != 0, sel_lds, tk);
+    if constexpr (COHERENT) {
+      const TaggedScores tw{reinterpret_cast<const uint64_t*>(a.pooled) + (size_t)bt * a.maxb, a.epoch,
+                            a.spin_limit};
+      nsel = block_topk<NT, true>([&](int i) { return 0.0f; }, [&](int i) { return bt_row[i]; }, pages, nvis,
+                                  a.top_k, a.keep_last != 0, sel_lds, tk, tw);
+      bool gave_up = false;
+#pragma unroll
+      for (int w = 0; w < W; w++) gave_up |= tk.stale[w] != 0;
+      if (gave_up) {  // the item's results are marked invalid
+        uint16_t* orow = a.out + ((size_t)bt * a.Hq + (size_t)g * a.grp) * kHeadDim;
+        for (int i = tid; i < a.grp * kHeadDim; i += NT) orow[i] = 0x7FC0;
+        if (a.lse && tid < a.grp) a.lse[(size_t)bt * a.Hq + g * a.grp + tid] = __builtin_nanf("");
+        if (g == 0 && a.sel && tid < a.top_k) a.sel[(size_t)bt * a.top_k + tid] = -1;
+        return;
+      }
+    } else {
+      nsel = block_topk<NT>([&](int i) { return src[i]; }, [&](int i) { return bt_row[i]; }, pages, nvis,
+                            a.top_k, a.keep_last != 0, sel_lds, tk);
+    }
     if (g == 0 && a.sel)
       for (int k = tid; k < a.top_k; k += NT) a.sel[(size_t)bt * a.top_k + k] = k < nsel ? sel_lds[k] : -1;
   } else {

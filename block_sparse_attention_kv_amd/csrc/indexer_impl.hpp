@@ -273,10 +273,14 @@ constexpr int indexer_occupancy(int kf, int hp, int tq) {
 // B + 1 ints. Wave w of the workgroup scans the global work blocks
 // [W * total / (4 nwg), (W + 1) * total / (4 nwg)), W = 4 wg + w, where the
 // work blocks of the batch are numbered sequence after sequence.
-// COHERENT: store the pooled scores as device-scope relaxed atomics (written
-// through to the device's coherence point, for readers in the same grid).
+// COHERENT: for readers in the same grid, every pooled score is stored as
+// one 64-bit word (tag << 32) | (fp32 bits) in a.pooled viewed as uint64
+// [B][Tq][maxb], with a device-scope relaxed atomic store (written through
+// to the device's coherence point); a reader that finds the call's tag in a
+// word holds that call's score.
 template <int KF, int HP, int TQ, bool SCORES, int NRING, bool COHERENT = false>
-__device__ __forceinline__ void indexer_body(const IndexerArgs& a, int32_t* prefix, int wg, int nwg) {
+__device__ __forceinline__ void indexer_body(const IndexerArgs& a, int32_t* prefix, int wg, int nwg,
+                                             uint32_t tag = 0) {
   typedef Shape<HP, TQ> S;
   static_assert(S::RT <= 2, "at most 32 query rows");
   __shared__ int32_t wsum[4];
@@ -427,9 +431,13 @@ __device__ __forceinline__ void indexer_body(const IndexerArgs& a, int32_t* pref
             for (int g2 = 0; g2 < 4; g2++) {
               const int t = 4 * tau + g2;
               if (t < a.Tq) {
-                float* dst = a.pooled + ((size_t)(b * a.Tq + t)) * a.maxb + w0 + lane;
-                if constexpr (COHERENT) __hip_atomic_store(dst, P[tau][g2], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                else *dst = P[tau][g2];
+                const size_t at = ((size_t)(b * a.Tq + t)) * a.maxb + w0 + lane;
+                if constexpr (COHERENT)
+                  __hip_atomic_store(reinterpret_cast<uint64_t*>(a.pooled) + at,
+                                     ((uint64_t)tag << 32) | __float_as_uint(P[tau][g2]), __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
+                else
+                  a.pooled[at] = P[tau][g2];
               }
             }
         }

@@ -97,12 +97,12 @@ msa_status_t check_cache_idx(const msa_params_t* p, const msa_cache_t* c) {
   return MSA_OK;
 }
 
-// Workspace: the pooled block scores, the completion flags of the indexer
-// workgroups (the single-launch layer) and, for small batches whose attention items are
-// split over several workgroups, the per-split softmax states and one
-// arrival word per item.
+// Workspace: the pooled block scores (8 bytes per entry: fp32 scores in the
+// two-kernel layer, tagged 64-bit words in the single-launch layer) and, for
+// small batches whose attention items are split over several workgroups,
+// the per-split softmax states and one arrival word per item.
 struct Layout {
-  size_t pooled_off, done_off, part_off, arrive_off, total;
+  size_t pooled_off, part_off, arrive_off, total;
   int splits;
 };
 // Only the bf16 path splits: its block loop has no prefetch, so a wave pays
@@ -120,8 +120,7 @@ Layout layout(const msa_params_t* p) {
   const size_t items = bt * p->num_kv_heads;
   L.splits = attn_splits(p);
   L.pooled_off = 0;
-  L.done_off = align256(bt * p->max_blocks_per_seq * sizeof(float));
-  L.part_off = L.done_off + align256((size_t)kLayerMaxIdxWgs * sizeof(uint32_t));
+  L.part_off = align256(bt * p->max_blocks_per_seq * sizeof(uint64_t));
   const size_t part = L.splits > 1 ? items * L.splits * 16 * kPartRow * sizeof(float) : 0;
   L.arrive_off = L.part_off + align256(part);
   L.total = L.arrive_off + (L.splits > 1 ? align256(items * sizeof(unsigned long long)) : 0);
@@ -228,6 +227,7 @@ AttnArgs attn_args(const msa_params_t* p, const msa_cache_t* c, const void* q, c
   a.partials = nullptr;
   a.arrivals = nullptr;
   a.epoch = 0;
+  a.spin_limit = 0;
   a.splits = 1;
   a.B = p->num_seqs;
   a.Tq = p->q_len;
@@ -372,8 +372,8 @@ msa_status_t msa_decode_layer_single_traced(const msa_params_t* p, const msa_cac
   AttnArgs aa = attn_args(p, c, q, pooled, sel_out, out, lse);
   set_splits(aa, p, nullptr, 0);  // one workgroup per item
   const KTimer tm = stage_timer(ev, 0);
-  hipError_t e = launch_layer_single(ia, aa, reinterpret_cast<uint32_t*>(ws + L.done_off), next_epoch(),
-                                     p->idx_dtype, p->idx_heads <= 4 ? 4 : 8, static_cast<hipStream_t>(stream), &tm);
+  hipError_t e = launch_layer_single(ia, aa, next_epoch(), p->idx_dtype, p->idx_heads <= 4 ? 4 : 8,
+                                     static_cast<hipStream_t>(stream), &tm);
   return e == hipSuccess ? MSA_OK : hip_fail(e, "single-launch layer");
 }
 

@@ -48,7 +48,9 @@ struct AttnArgs {
   float* lse;               // [B][Tq][Hq] or nullptr
   float* partials;          // [items][splits][16][kPartRow] softmax states (splits > 1)
   unsigned long long* arrivals;  // [items]: (epoch << 32) | workgroups arrived (splits > 1)
-  uint32_t epoch;           // distinct per call: older arrival words count as zero
+  uint32_t epoch;           // distinct per call: older arrival words count as zero; the
+                            // single launch's tag of the pooled scores
+  int spin_limit;           // single launch: polls of a pooled score before an item gives up
   int splits;               // workgroups per (sequence, token, KV head) item
   float score_scale;        // softmax_scale * log2(e) * k_tensor_scale
   float v_scale_mul;        // v_tensor_scale
@@ -102,11 +104,11 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t s);
 hipError_t launch_insert(const InsertArgs& a, hipStream_t s);
 hipError_t launch_attn(const AttnArgs& a, bool nvfp4, int waves, hipStream_t s, const KTimer* t = nullptr);
 // The decode layer as one launch (layer.hip); NVFP4 K/V, FP8 or NVFP4
-// indexer keys, q_len <= 4. wg_done: kLayerMaxIdxWgs flag words; epoch:
-// distinct per call.
+// indexer keys, q_len <= 4. ia.pooled / aa.pooled: the workspace's pooled
+// scores, 8 bytes per entry; epoch: distinct per call.
 constexpr int kLayerMaxIdxWgs = 4096;
-hipError_t launch_layer_single(const IndexerArgs& ia, const AttnArgs& aa, uint32_t* wg_done, uint32_t epoch,
-                               int key_format, int hp, hipStream_t s, const KTimer* t = nullptr);
+hipError_t launch_layer_single(const IndexerArgs& ia, const AttnArgs& aa, uint32_t epoch, int key_format, int hp,
+                               hipStream_t s, const KTimer* t = nullptr);
 // Poll limit of the single-launch layer's waits for later launches (0: the
 // default of about a second).
 void set_layer_spin_limit(int polls);

@@ -29,7 +29,18 @@ constexpr int kTopkCap = 16;  // k <= 16
 struct TopkLds {
   uint64_t win[16][kTopkCap];  // [wave][slot]
   int32_t nwin[16];
+  int32_t stale[16];           // [wave]: tagged scores still absent at the poll limit
   uint64_t fin[kTopkCap];
+};
+
+// Scores published by other workgroups of the same grid as 64-bit words
+// (tag << 32) | (fp32 bits): a word holds a valid score once its high half
+// equals `tag`. src[i] is block i's word; a missing word is read again,
+// `limit` polls at most.
+struct TaggedScores {
+  const uint64_t* src;
+  uint32_t tag;
+  int limit;
 };
 
 __device__ __forceinline__ uint64_t block_key(float v, int i, bool forced) {
@@ -46,16 +57,27 @@ __device__ __forceinline__ int count_ge(const uint64_t (&k)[NK], uint64_t c) {
   return n;
 }
 
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) v = max(v, (uint32_t)shfl_xor((int)v, m));
-  return v;
+// Max (MAX) or min of v over the 64 lanes, returned uniform. DPP moves keep
+// the reduction in registers: shifts by 1, 2, 4 and 8 lanes within each row
+// of 16 (a lane with no source lane takes the identity) leave the row's
+// extremum in its lane 15; row_bcast:15 folds row 0 into row 1 and row 2
+// into row 3, row_bcast:31 folds lane 31 into rows 2 and 3, so lane 63 holds
+// the result. (A shuffle-based butterfly costs an LDS-crossbar round trip
+// per step.)
+template <bool MAX>
+__device__ __forceinline__ uint32_t wave_extremum_u32(uint32_t v) {
+  constexpr int id = MAX ? 0 : -1;
+  auto op = [](uint32_t x, int y) { return MAX ? max(x, (uint32_t)y) : min(x, (uint32_t)y); };
+  v = op(v, __builtin_amdgcn_update_dpp(id, (int)v, 0x111, 0xF, 0xF, false));  // row_shr:1
+  v = op(v, __builtin_amdgcn_update_dpp(id, (int)v, 0x112, 0xF, 0xF, false));  // row_shr:2
+  v = op(v, __builtin_amdgcn_update_dpp(id, (int)v, 0x114, 0xF, 0xF, false));  // row_shr:4
+  v = op(v, __builtin_amdgcn_update_dpp(id, (int)v, 0x118, 0xF, 0xF, false));  // row_shr:8
+  v = op(v, __builtin_amdgcn_update_dpp(id, (int)v, 0x142, 0xA, 0xF, false));  // row_bcast:15 -> rows 1, 3
+  v = op(v, __builtin_amdgcn_update_dpp(id, (int)v, 0x143, 0xC, 0xF, false));  // row_bcast:31 -> rows 2, 3
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
-__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) v = min(v, (uint32_t)shfl_xor((int)v, m));
-  return v;
-}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) { return wave_extremum_u32<true>(v); }
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) { return wave_extremum_u32<false>(v); }
 
 // Threshold T with exactly K keys >= T, K <= number of nonzero keys (keys
 // are unique). Returns T (uniform).
@@ -123,9 +145,15 @@ __device__ __forceinline__ void compact_ge(const uint64_t (&k)[NK], uint64_t T, 
 // side load of the same pass. All NT threads (a multiple of 64, at most 1024)
 // call it; it ends with a barrier, after which out[] and pages[] are visible
 // to all of them.
-template <int NT, typename ScoreFn, typename PageFn>
+//
+// TAGGED: the scores come from tw (score is unused) and are read with
+// device-scope atomic loads; a chunk's missing words are polled again (a
+// short sleep between polls) until present or until tw.limit polls. Then
+// s.stale[w] = 1 for every wave w that gave up (the selection is then
+// meaningless), else 0 (also when n <= top_k: no score is read).
+template <int NT, bool TAGGED = false, typename ScoreFn, typename PageFn>
 __device__ int block_topk(ScoreFn score, PageFn page, int32_t* pages, int n, int top_k, bool keep_last,
-                          int32_t* out, TopkLds& s) {
+                          int32_t* out, TopkLds& s, TaggedScores tw = TaggedScores{nullptr, 0u, 0}) {
   static_assert(NT % 64 == 0 && NT <= 1024, "workgroup size");
   constexpr int NW = NT / 64;
   const int lane = lane_id();
@@ -135,29 +163,64 @@ __device__ int block_topk(ScoreFn score, PageFn page, int32_t* pages, int n, int
       out[k] = k;
       if (pages) pages[k] = page(k);
     }
+    if (lane == 0) s.stale[wave] = 0;
     __syncthreads();
     return n < 0 ? 0 : n;
   }
   // ---- this wave's share: blocks [lo, hi), in chunks of 256 (4 per lane)
   const int per = (n + NW - 1) / NW;
   const int lo = min(n, wave * per), hi = min(n, lo + per);
+  // TAGGED: the raw words of a chunk are requested first (wv) and turned into
+  // scores (v) only when the chunk is searched, after the next chunk's
+  // requests are out
   float v[4];
+  uint64_t wv[4];
   int pg[4];
-  auto fetch = [&](int base, float (&vv)[4], int (&pp)[4]) {
+  bool stale = false;
+  const uint64_t absent_ok = (uint64_t)tw.tag << 32;  // score 0 with the expected tag
+  auto fetch = [&](int base, float (&vv)[4], uint64_t (&ww)[4], int (&pp)[4]) {
 #pragma unroll
     for (int j = 0; j < 4; j++) {
       const int i = base + 64 * j + lane;
-      vv[j] = i < hi ? score(i) : 0.0f;
+      if constexpr (TAGGED)
+        ww[j] = i < hi ? __hip_atomic_load(tw.src + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : absent_ok;
+      else
+        vv[j] = i < hi ? score(i) : 0.0f;
       if (pages) pp[j] = i < hi ? page(i) : -1;
     }
   };
-  if (lo < hi) fetch(lo, v, pg);
+  auto settle = [&](int base) {
+    if constexpr (TAGGED) {
+      for (int polls = 0;;) {
+        bool miss = false;
+#pragma unroll
+        for (int j = 0; j < 4; j++) miss |= (uint32_t)(wv[j] >> 32) != tw.tag;
+        if (__ballot(miss) == 0ull) break;
+        if (++polls >= tw.limit) {
+          stale = true;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          const int i = base + 64 * j + lane;
+          if ((uint32_t)(wv[j] >> 32) != tw.tag)
+            wv[j] = __hip_atomic_load(tw.src + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 4; j++) v[j] = __uint_as_float((uint32_t)wv[j]);
+    }
+  };
+  if (lo < hi) fetch(lo, v, wv, pg);
   uint64_t carry = 0;  // lanes 0..nc-1: current winners
   int nc = 0;
   for (int base = lo; base < hi; base += 256) {
     float vn[4];
+    uint64_t wn[4];
     int pn[4];
-    if (base + 256 < hi) fetch(base + 256, vn, pn);
+    if (base + 256 < hi) fetch(base + 256, vn, wn, pn);
+    settle(base);
     uint64_t k[5];
 #pragma unroll
     for (int j = 0; j < 4; j++) {
@@ -180,11 +243,15 @@ __device__ int block_topk(ScoreFn score, PageFn page, int32_t* pages, int n, int
     wave_lds_sync();
 #pragma unroll
     for (int j = 0; j < 4; j++) {
-      v[j] = vn[j];
+      if constexpr (TAGGED) wv[j] = wn[j];
+      else v[j] = vn[j];
       pg[j] = pn[j];
     }
   }
-  if (lane == 0) s.nwin[wave] = nc;
+  if (lane == 0) {
+    s.nwin[wave] = nc;
+    s.stale[wave] = stale ? 1 : 0;
+  }
   __syncthreads();
   // ---- wave 0: top_k of all waves' winners (at most 16 x 16), then sort
   if (wave == 0) {

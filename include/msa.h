@@ -239,16 +239,18 @@ msa_status_t msa_decode_layer_traced(const msa_params_t* p, const msa_cache_t* c
 /* msa_decode_layer as ONE kernel launch on `stream` [upstreambeat page
  * "vLLM turns MiniMax's day-zero promise into GPU-specific serving code",
  * section "What changed": a single-launch ("mono") decode path on MI355X to
- * cut launch overhead]: the indexer and pooling phase, a grid-wide barrier,
- * then selection and attention. Same arguments, workspace and selection as
- * msa_decode_layer; its attention always runs 4 waves per (sequence, token,
- * KV head), so out and lse equal msa_decode_layer's bit for bit when the
- * batch has at least two such items per compute unit (below that,
- * msa_decode_layer spreads an item over 8 waves and the rounding of the
- * merge differs). The grid is cooperative (two workgroups per
- * compute unit, all resident at once), so it must not share the device with
- * work that keeps those slots busy, and a device without cooperative launch
- * returns MSA_ERR_HIP. Supported: kv_dtype MSA_KV_NVFP4, idx_dtype
+ * cut launch overhead]: the first workgroups of the grid run the indexer
+ * and pooling phase and publish every pooled score tagged with the call's
+ * epoch; the others, one per (sequence, token, KV head), each wait for the
+ * tagged scores of their query token, then select and attend. Same
+ * arguments, workspace and selection as msa_decode_layer; its attention
+ * always runs 4 waves per (sequence, token, KV head), so out and lse equal
+ * msa_decode_layer's bit for bit when the batch has at least two such items
+ * per compute unit (below that, msa_decode_layer spreads an item over 8
+ * waves and the rounding of the merge differs). Attention workgroups are
+ * dispatched after every indexer workgroup and indexer workgroups wait on
+ * nothing, so every wait ends; each wait is also bounded (see
+ * msa_debug_layer_spin_limit). Supported: kv_dtype MSA_KV_NVFP4, idx_dtype
  * MSA_IDX_FP8_E4M3 or MSA_IDX_NVFP4, q_len <= 4; other valid problems return
  * MSA_ERR_UNSUPPORTED before anything is enqueued. */
 msa_status_t msa_decode_layer_single(const msa_params_t* p, const msa_cache_t* cache,
@@ -309,10 +311,11 @@ msa_status_t msa_debug_dequant_fp8(const uint8_t* codes, int64_t n, float* out,
                                    void* stream);
 
 /* Debug export: the number of polls after which a workgroup of
- * msa_decode_layer_single stops waiting for the indexer workgroups that
- * cover its sequence (default, polls = 0: about a second of polling). An
- * item that stops writes NaN to its out rows and lse entries and -1 to its
- * selection; the kernel still ends normally. Applies to later calls in this
+ * msa_decode_layer_single stops waiting for the pooled scores of its query
+ * token (default, polls = 0: about a second of polling; with polls = 1 an
+ * item gives up as soon as one score of a chunk it reads is not yet
+ * published). An item that stops writes NaN to its out rows and lse entries
+ * and -1 to its selection; the kernel still ends normally. Applies to later calls in this
  * process; polls < 0 returns MSA_ERR_INVALID_ARG. For tests of the bounded
  * wait. */
 msa_status_t msa_debug_layer_spin_limit(int32_t polls);

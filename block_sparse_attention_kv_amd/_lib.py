@@ -223,8 +223,8 @@ def msa_decode_layer(params, cache, q, idx_q, idx_w, out, workspace, lse=None, s
 
 
 def msa_decode_layer_single(params, cache, q, idx_q, idx_w, out, workspace, lse=None, sel_out=None, stream=None):
-    """msa_decode_layer in one cooperative kernel launch (NVFP4 K/V, FP8 or
-    NVFP4 indexer keys, q_len <= 4)."""
+    """msa_decode_layer in one kernel launch (NVFP4 K/V, FP8 or NVFP4
+    indexer keys, q_len <= 4)."""
     c = cache.c()
     ws_bytes = workspace.numel() * workspace.element_size()
     _check(load().msa_decode_layer_single(ctypes.byref(params), ctypes.byref(c), _ptr(q), _ptr(idx_q), _ptr(idx_w),

@@ -89,6 +89,40 @@ def test_single_repeat_reuses_workspace():
         assert np.array_equal(first["sel"], again["sel"])
 
 
+def test_single_workspace_holds_no_stale_scores():
+    # Two different batches of one shape alternate through one workspace.
+    # The pooled scores a call reads must be its own, not the words the
+    # other batch's call left there (they carry another call's tag), so
+    # every result equals that batch's run on a fresh zero-filled workspace
+    # bit for bit.
+    lens = [5000, 2100, 3300, 700]
+    wa = make_workload("ws_a", 71, lens, 4, 16, 2, 8, KV_NVFP4, IDX_FP8, table="permute")
+    wb = make_workload("ws_b", 72, lens, 4, 16, 2, 8, KV_NVFP4, IDX_FP8, table="permute")
+    assert wa.params == wb.params
+    ra, rb = G.Run(wa), G.Run(wb)
+    prm = wa.params
+    B, Tq, Hq, K = prm["num_seqs"], prm["q_len"], prm["num_q_heads"], prm["top_k"]
+
+    def call(r, ws):
+        out = torch.empty((B, Tq, Hq, 128), dtype=torch.int16, device="cuda")
+        lse = torch.empty((B, Tq, Hq), dtype=torch.float32, device="cuda")
+        sel = torch.empty((B, Tq, K), dtype=torch.int32, device="cuda")
+        msa.msa_decode_layer_single(r.params, r.cache, r.q, r.idx_q, r.idx_w, out, ws, lse=lse, sel_out=sel)
+        torch.cuda.synchronize()
+        return out.cpu().numpy(), lse.cpu().numpy(), sel.cpu().numpy()
+
+    want = {}
+    for key, r in (("a", ra), ("b", rb)):
+        fresh = msa.alloc_workspace(r.params, "cuda").zero_()
+        want[key] = call(r, fresh)
+    assert not np.array_equal(want["a"][2], want["b"][2])  # the batches select differently
+    ws = msa.alloc_workspace(ra.params, "cuda")
+    for key, r in (("a", ra), ("b", rb), ("a", ra), ("b", rb), ("b", rb)):
+        got = call(r, ws)
+        for g, x in zip(got, want[key]):
+            assert np.array_equal(g.view(np.uint8), x.view(np.uint8)), key
+
+
 @pytest.mark.parametrize("cfg,idx", [(2, IDX_FP8), (3, IDX_FP8), (3, IDX_NVFP4), (4, IDX_FP8), (5, IDX_FP8)])
 def test_single_full_size(cfg, idx):
     # the decode configurations at full size (32K x 8, the 128K speculative

@@ -39,6 +39,9 @@ METRIC = "MSA decode tokens/s per layer at 128K ctx; achieved HBM GB/s vs 8 TB/s
 ROOT = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(ROOT, "block_sparse_attention_kv_amd", "csrc")
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "traffic.json")
+# --layer auto: indexer bytes per step up to which the single launch is
+# taken whatever the number of attention items
+SINGLE_SCAN_BYTES = 64e6
 # the files each kernel's device code is compiled from (a traffic record is
 # valid only for the sources it was taken on)
 KERNELS = {
@@ -208,7 +211,8 @@ def main():
                     help="only run this many steps and a 1 GiB calibration copy (for rocprofv3 runs)")
     ap.add_argument("--layer", choices=("auto", "single", "two"), default="auto",
                     help="single: msa_decode_layer_single; two: msa_decode_layer; auto: single where it applies "
-                         "and has at least two (sequence, token, KV head) items per compute unit")
+                         "and has at least two (sequence, token, KV head) items per compute unit or a short "
+                         "indexer scan (<= 64 MB)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write a record of profiles/traffic.json from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE "
                          "counter collections of a --profile-steps run, and exit")
@@ -267,7 +271,10 @@ def main():
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     single_ok = prm["kv_dtype"] == 1 and prm["idx_dtype"] in (1, 2) and Tq <= 4
     if args.layer == "auto":
-        single = single_ok and items >= 2 * cus
+        # the single launch wins from two items per CU up, and wherever the
+        # scan is short enough that the gap between two kernels weighs more
+        # than 4 instead of 8 waves per item (measured: 32K x 8 sequences)
+        single = single_ok and (items >= 2 * cus or indexer_bytes(w) <= SINGLE_SCAN_BYTES)
     else:
         single = args.layer == "single"
         if single and not single_ok:

@@ -259,5 +259,7 @@ def msa_debug_dequant_fp8(codes, out, stream=None):
 
 
 def alloc_workspace(params, device="cuda"):
+    """Workspace for the decode calls, zero-filled once (the single-launch
+    layer's tagged scores then cannot match a call's tag by accident)."""
     n = msa_workspace_size(params)
-    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+    return torch.zeros(max(n, 256), dtype=torch.uint8, device=device)

@@ -97,12 +97,13 @@ msa_status_t check_cache_idx(const msa_params_t* p, const msa_cache_t* c) {
   return MSA_OK;
 }
 
-// Workspace: the pooled block scores (8 bytes per entry: fp32 scores in the
-// two-kernel layer, tagged 64-bit words in the single-launch layer) and, for
+// Workspace: the pooled block scores of the two-kernel layer (fp32), those
+// of the single-launch layer (tagged 64-bit words, a region of their own so
+// that no fp32 pair the other layer left can pass for a tagged word) and, for
 // small batches whose attention items are split over several workgroups,
 // the per-split softmax states and one arrival word per item.
 struct Layout {
-  size_t pooled_off, part_off, arrive_off, total;
+  size_t pooled_off, tagged_off, part_off, arrive_off, total;
   int splits;
 };
 // Only the bf16 path splits: its block loop has no prefetch, so a wave pays
@@ -120,7 +121,8 @@ Layout layout(const msa_params_t* p) {
   const size_t items = bt * p->num_kv_heads;
   L.splits = attn_splits(p);
   L.pooled_off = 0;
-  L.part_off = align256(bt * p->max_blocks_per_seq * sizeof(uint64_t));
+  L.tagged_off = align256(bt * p->max_blocks_per_seq * sizeof(float));
+  L.part_off = L.tagged_off + align256(bt * p->max_blocks_per_seq * sizeof(uint64_t));
   const size_t part = L.splits > 1 ? items * L.splits * 16 * kPartRow * sizeof(float) : 0;
   L.arrive_off = L.part_off + align256(part);
   L.total = L.arrive_off + (L.splits > 1 ? align256(items * sizeof(unsigned long long)) : 0);
@@ -133,7 +135,10 @@ Layout layout(const msa_params_t* p) {
 uint32_t next_epoch() {
   static std::atomic<uint32_t> ctr{0};
   static const uint32_t base = (uint32_t)std::chrono::steady_clock::now().time_since_epoch().count() * 2654435761u;
-  return base + ctr.fetch_add(1, std::memory_order_relaxed) + 1u;
+  for (;;) {  // never 0: zero-filled memory then holds no call's tag
+    const uint32_t e = base + ctr.fetch_add(1, std::memory_order_relaxed) + 1u;
+    if (e != 0u) return e;
+  }
 }
 
 // Splits the attention of small batches when the workspace has room.
@@ -366,7 +371,7 @@ msa_status_t msa_decode_layer_single_traced(const msa_params_t* p, const msa_cac
   if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
     return fail(MSA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
   uint8_t* ws = static_cast<uint8_t*>(workspace);
-  float* pooled = reinterpret_cast<float*>(ws + L.pooled_off);
+  float* pooled = reinterpret_cast<float*>(ws + L.tagged_off);  // tagged 64-bit words
   IndexerArgs ia = indexer_args(p, c, idx_q, idx_w);
   ia.pooled = pooled;
   AttnArgs aa = attn_args(p, c, q, pooled, sel_out, out, lse);

@@ -252,7 +252,13 @@ msa_status_t msa_decode_layer_traced(const msa_params_t* p, const msa_cache_t* c
  * nothing, so every wait ends; each wait is also bounded (see
  * msa_debug_layer_spin_limit). Supported: kv_dtype MSA_KV_NVFP4, idx_dtype
  * MSA_IDX_FP8_E4M3 or MSA_IDX_NVFP4, q_len <= 4; other valid problems return
- * MSA_ERR_UNSUPPORTED before anything is enqueued. */
+ * MSA_ERR_UNSUPPORTED before anything is enqueued. Workspace: the tagged
+ * scores sit in a region of their own, and a word counts only when its tag
+ * equals the call's epoch (a per-call 32-bit value, never 0). Words the
+ * library wrote in earlier calls never match; memory it never wrote matches
+ * with probability about 2^-32 per word, so a workspace should be
+ * zero-filled once before its first use (the Python binding's
+ * alloc_workspace does) — no clearing is needed between calls. */
 msa_status_t msa_decode_layer_single(const msa_params_t* p, const msa_cache_t* cache,
                                      const void* q, const void* idx_q, const float* idx_w,
                                      void* out, float* lse, int32_t* sel_out,

@@ -121,6 +121,17 @@ def test_single_workspace_holds_no_stale_scores():
         got = call(r, ws)
         for g, x in zip(got, want[key]):
             assert np.array_equal(g.view(np.uint8), x.view(np.uint8)), key
+    # the two-kernel layer on the same workspace between single launches
+    # leaves its own (fp32) pooled scores, which the single launch must not
+    # read: its results stay those of a fresh workspace
+    for key, r in (("a", ra), ("b", rb), ("a", ra)):
+        out = torch.empty((B, Tq, Hq, 128), dtype=torch.int16, device="cuda")
+        msa.msa_decode_layer(r.params, r.cache, r.q, r.idx_q, r.idx_w, out, ws)
+        other = rb if r is ra else ra
+        got = call(other, ws)
+        okey = "b" if key == "a" else "a"
+        for g, x in zip(got, want[okey]):
+            assert np.array_equal(g.view(np.uint8), x.view(np.uint8)), okey
 
 
 @pytest.mark.parametrize("cfg,idx", [(2, IDX_FP8), (3, IDX_FP8), (3, IDX_NVFP4), (4, IDX_FP8), (5, IDX_FP8)])

@@ -50,6 +50,13 @@ def test_workspace_size():
     n = msa.msa_workspace_size(p)
     assert n >= 4 * 1 * 1 * 32 and n % 256 == 0
     assert msa.msa_workspace_size(_params(head_dim=64)) == 0
+    # fp32 pooled scores of the two-kernel layer plus the single launch's
+    # tagged 64-bit words, each in a 256-byte aligned region of its own
+    for B, Tq, maxb in ((32, 4, 1024), (3, 2, 17), (1, 1, 1)):
+        q = _params(num_seqs=B, q_len=Tq, max_blocks_per_seq=maxb, num_pages=B * maxb)
+        entries = B * Tq * maxb
+        align = lambda x: (x + 255) // 256 * 256
+        assert msa.msa_workspace_size(q) >= align(4 * entries) + align(8 * entries)
 
 
 @pytest.mark.parametrize("over,status", [

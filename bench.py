@@ -362,6 +362,18 @@ def main():
     c1.record()
     torch.cuda.synchronize()
     copy_gbps = 2 * (1 << 30) * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    # ---- attainable read bandwidth: the library's streaming read kernel
+    chk = torch.zeros(4, dtype=torch.int32, device=dev)
+    for _ in range(3):
+        msa.msa_debug_read_bandwidth(src, chk)
+    c0.record()
+    for _ in range(10):
+        msa.msa_debug_read_bandwidth(src, chk)
+    c1.record()
+    torch.cuda.synchronize()
+    read_gbps = (1 << 30) * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    log("attainable on this box: read %.0f GB/s (1 GiB stream), device copy %.0f GB/s (read + write)"
+        % (read_gbps, copy_gbps))
     del src, dst
 
     idx_b = indexer_bytes(w)
@@ -403,7 +415,8 @@ def main():
         "step": dict({"entry": entry, "algorithmic_bytes": step_b, "gbps": step_gbps,
                       "frac": step_gbps / HBM_PEAK_GBPS, "stage_ms": dict(zip(stage_names, stage_ms)),
                       "ms_per_step_with_kernel_events": ms_step_traced, "indexer_bytes": idx_b,
-                      "attention_bytes": att_b, "copy_gbps_attainable": copy_gbps}, **stage_detail),
+                      "attention_bytes": att_b, "copy_gbps_attainable": copy_gbps,
+                      "read_gbps_attainable": read_gbps}, **stage_detail),
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, gpu_res, args.cpu_budget)

@@ -83,6 +83,7 @@ def load():
         "msa_kv_insert": (st, [P, C, vp, vp, vp, vp]),
         "msa_debug_dequant_nvfp4": (st, [vp, vp, i64, vp, vp]),
         "msa_debug_dequant_fp8": (st, [vp, i64, vp, vp]),
+        "msa_debug_read_bandwidth": (st, [vp, i64, vp, vp]),
         "msa_debug_layer_spin_limit": (st, [ctypes.c_int32]),
         "msa_status_string": (ctypes.c_char_p, [st]),
         "msa_last_error": (ctypes.c_char_p, []),
@@ -99,7 +100,7 @@ def load():
 EXPORTED = ("msa_workspace_size", "msa_indexer_scores", "msa_pool_select_blocks", "msa_sparse_attn_decode",
             "msa_decode_layer", "msa_decode_layer_traced", "msa_decode_layer_single",
             "msa_decode_layer_single_traced", "msa_kv_insert", "msa_debug_dequant_nvfp4",
-            "msa_debug_dequant_fp8", "msa_debug_layer_spin_limit",
+            "msa_debug_dequant_fp8", "msa_debug_read_bandwidth", "msa_debug_layer_spin_limit",
             "msa_status_string", "msa_last_error", "msa_version")
 
 
@@ -256,6 +257,14 @@ def msa_debug_layer_spin_limit(polls):
 def msa_debug_dequant_fp8(codes, out, stream=None):
     _check(load().msa_debug_dequant_fp8(_ptr(codes), codes.numel(), _ptr(out), _stream(stream)),
            "msa_debug_dequant_fp8")
+
+
+def msa_debug_read_bandwidth(buf, out, stream=None):
+    """Stream the device tensor `buf` (a multiple of 16 bytes) through the
+    library's read kernel; out: a device tensor of at least 4 bytes."""
+    nbytes = buf.numel() * buf.element_size()
+    _check(load().msa_debug_read_bandwidth(_ptr(buf), nbytes, _ptr(out), _stream(stream)),
+           "msa_debug_read_bandwidth")
 
 
 def alloc_workspace(params, device="cuda"):

@@ -258,6 +258,11 @@ KTimer stage_timer(void* const* ev, int i) {
 
 }  // namespace
 
+namespace msa {
+// Streaming read of `bytes` (a multiple of 16) of device memory (debug.hip).
+hipError_t launch_debug_read(const void* buf, int64_t bytes, uint32_t* out, int cus, hipStream_t s);
+}  // namespace msa
+
 extern "C" {
 
 size_t msa_workspace_size(const msa_params_t* p) {
@@ -465,6 +470,15 @@ msa_status_t msa_debug_dequant_fp8(const uint8_t* codes, int64_t n, float* out, 
   if (n > 0 && (!codes || !out)) return fail(MSA_ERR_INVALID_ARG, "NULL buffer");
   if (n > (int64_t)0xFFFFFFFF * 2048) return fail(MSA_ERR_UNSUPPORTED, "n too large");
   hipError_t e = launch_debug_fp8(codes, n, out, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MSA_OK : hip_fail(e, "debug launch");
+}
+
+msa_status_t msa_debug_read_bandwidth(const void* buf, int64_t bytes, uint32_t* out, void* stream) {
+  g_err[0] = 0;
+  if (bytes < 0 || bytes % 16 != 0) return fail(MSA_ERR_INVALID_ARG, "bytes must be a non-negative multiple of 16");
+  if (bytes > 0 && (!buf || !out)) return fail(MSA_ERR_INVALID_ARG, "NULL buffer");
+  if ((reinterpret_cast<uintptr_t>(buf) & 15) != 0) return fail(MSA_ERR_INVALID_ARG, "buf must be 16-byte aligned");
+  hipError_t e = launch_debug_read(buf, bytes, out, device_cus(), static_cast<hipStream_t>(stream));
   return e == hipSuccess ? MSA_OK : hip_fail(e, "debug launch");
 }
 

@@ -316,6 +316,18 @@ msa_status_t msa_debug_dequant_nvfp4(const uint8_t* codes, const uint8_t* scales
 msa_status_t msa_debug_dequant_fp8(const uint8_t* codes, int64_t n, float* out,
                                    void* stream);
 
+/* Measurement export: streams `bytes` of device memory at `buf` (16-byte
+ * aligned, bytes a multiple of 16) with 16-byte nontemporal loads, 4 KB of
+ * contiguous memory per wave and step, 16 waves per compute unit, so that
+ * the time of the call on `stream` gives the
+ * device's attainable read bandwidth, the ceiling that the decode kernels'
+ * rates are read against beside the nominal HBM peak. `out`: 4 bytes of
+ * device memory the kernel may write (a checksum of the data; stored only
+ * when it equals a fixed value, so that the loads stay and nothing is
+ * written in practice). Errors: MSA_ERR_INVALID_ARG for a NULL buffer
+ * (bytes > 0), a misaligned buf or a size not a multiple of 16. */
+msa_status_t msa_debug_read_bandwidth(const void* buf, int64_t bytes, uint32_t* out, void* stream);
+
 /* Debug export: the number of polls after which a workgroup of
  * msa_decode_layer_single stops waiting for the pooled scores of its query
  * token (default, polls = 0: about a second of polling; with polls = 1 an

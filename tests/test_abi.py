@@ -105,6 +105,12 @@ def test_null_pointers_rejected():
         _lib.MSA_ERR_INVALID_ARG
     assert L.msa_debug_dequant_nvfp4(None, None, 4, None, None) == _lib.MSA_ERR_INVALID_ARG
     assert L.msa_debug_dequant_fp8(None, -1, None, None) == _lib.MSA_ERR_INVALID_ARG
+    assert L.msa_debug_read_bandwidth(None, 64, None, None) == _lib.MSA_ERR_INVALID_ARG
+    assert L.msa_debug_read_bandwidth(None, 17, None, None) == _lib.MSA_ERR_INVALID_ARG
+    assert L.msa_debug_read_bandwidth(None, -16, None, None) == _lib.MSA_ERR_INVALID_ARG
+    assert L.msa_debug_read_bandwidth(ctypes.c_void_p(8), 64, ctypes.c_void_p(16), None) == _lib.MSA_ERR_INVALID_ARG
+    assert "aligned" in L.msa_last_error().decode()
+    assert L.msa_debug_read_bandwidth(None, 0, None, None) == _lib.MSA_OK  # nothing to read, no launch
 
 
 def test_dtype_scale_consistency_rejected():

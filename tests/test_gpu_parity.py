@@ -161,3 +161,15 @@ def test_split_attention_reuses_workspace():
         outs.append((out.cpu().numpy(), sel.cpu().numpy()))
     assert all(np.array_equal(o[0], outs[0][0]) and np.array_equal(o[1], outs[0][1]) for o in outs)
     G.layer_parity(w, run=run)
+
+
+def test_read_bandwidth_kernel_reads_and_writes_nothing():
+    # the measurement kernel streams the buffer (a size that leaves a tail
+    # after the unrolled grid-stride loop) and stores nothing: the XOR of a
+    # zero buffer never equals its store condition
+    buf = torch.zeros((1 << 20) + 48, dtype=torch.uint8, device="cuda")
+    chk = torch.full((4,), 7, dtype=torch.int32, device="cuda")
+    msa.msa_debug_read_bandwidth(buf, chk)
+    msa.msa_debug_read_bandwidth(buf[:0], chk)
+    torch.cuda.synchronize()
+    assert chk.cpu().tolist() == [7, 7, 7, 7]

@@ -345,10 +345,15 @@ def main():
     k1.record()
     torch.cuda.synchronize()
     ms_step_traced = k0.elapsed_time(k1) / args.steps
-    stage_ms = [float(np.mean([kev[i][2 * s].elapsed_time(kev[i][2 * s + 1]) for i in range(args.steps)]))
-                for s in range(n_st)]
+    stage_all = [np.array([kev[i][2 * s].elapsed_time(kev[i][2 * s + 1]) for i in range(args.steps)])
+                 for s in range(n_st)]
+    stage_ms = [float(np.mean(d)) for d in stage_all]
+    # spread of the per-step kernel durations (ms): p10, median, p90
+    stage_pct = {n: [float(x) for x in np.percentile(d, [10, 50, 90])] for n, d in zip(stage_names, stage_all)}
     log("kernels (ms): " + ", ".join("%s %.4f" % (n, v) for n, v in zip(stage_names, stage_ms)) +
         "; step with kernel events %.4f ms" % ms_step_traced)
+    log("kernel durations p10 / median / p90 (ms): " +
+        ", ".join("%s %.4f / %.4f / %.4f" % (n, *stage_pct[n]) for n in stage_names))
 
     # ---- attainable copy bandwidth on this machine (context)
     src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -414,6 +419,7 @@ def main():
                      "algorithmic_bytes": kern_b, "avg_ms": kern_ms},
         "step": dict({"entry": entry, "algorithmic_bytes": step_b, "gbps": step_gbps,
                       "frac": step_gbps / HBM_PEAK_GBPS, "stage_ms": dict(zip(stage_names, stage_ms)),
+                      "stage_ms_p10_p50_p90": stage_pct,
                       "ms_per_step_with_kernel_events": ms_step_traced, "indexer_bytes": idx_b,
                       "attention_bytes": att_b, "copy_gbps_attainable": copy_gbps,
                       "read_gbps_attainable": read_gbps}, **stage_detail),

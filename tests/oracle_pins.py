@@ -305,3 +305,52 @@ def check_causal_positions(O, w):
         L = int(w.ctx_lens[b])
         if L <= 16 * 128:
             assert res[-1]["n_keys"] == L
+
+
+def _rank_by_dominance(Pk):
+    """rank[i] = number of blocks that beat block i under (score desc, index
+    asc), counted pair by pair (no sort)."""
+    n = len(Pk)
+    return [sum(1 for j in range(n) if _dominates(Pk, j, i)) for i in range(n)]
+
+
+def check_boundary_bruteforce(O, seed=6):
+    """boundary_values(P, k, keep_last) = (the score ranked k-th, the score
+    ranked (k+1)-th) of the keep-last-adjusted pooled scores, ranks counted by
+    pairwise dominance; (None, None) when every block is selected. Also: the
+    k-th value is the smallest adjusted score inside the selected set and the
+    (k+1)-th the largest outside it."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for n in (2, 5, 16, 17, 18, 23, 40):
+        for trial in range(3):
+            if trial == 0:
+                P = rng.integers(0, 4, size=n).astype(np.float64)     # exact ties
+            elif trial == 1:
+                P = rng.normal(size=n)
+            else:
+                P = np.full(n, 0.5)                                    # all tied
+            cases.append(P)
+    cases.append(np.array([3.0, -1.0, 7.0, 7.0, -np.inf, 2.0, 7.0, 0.0, 1.0, 5.0]))
+    for P in cases:
+        n = len(P)
+        for top_k in (1, 2, 4, 16):
+            for keep_last in (True, False):
+                got = O.boundary_values(P, top_k, keep_last)
+                if n <= top_k:
+                    assert got == (None, None), (P, top_k, keep_last, got)
+                    continue
+                Pk = [float(x) for x in P]
+                if keep_last:
+                    Pk[-1] = math.inf
+                rank = _rank_by_dominance(Pk)
+                want_k = [Pk[i] for i in range(n) if rank[i] == top_k - 1]
+                want_k1 = [Pk[i] for i in range(n) if rank[i] == top_k]
+                assert len(want_k) == 1 and len(want_k1) == 1
+                assert got == (want_k[0], want_k1[0]), (list(P), top_k, keep_last, got, want_k, want_k1)
+                # values only: the k-th / (k+1)-th of the adjusted scores sorted descending
+                srt = sorted(Pk, reverse=True)
+                assert got == (srt[top_k - 1], srt[top_k])
+                S = set(int(i) for i in O.select_blocks(P, top_k, keep_last))
+                assert got[0] == min(Pk[i] for i in S)
+                assert got[1] == max(Pk[i] for i in range(n) if i not in S)

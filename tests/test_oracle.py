@@ -117,3 +117,7 @@ def test_config1_invariants():
     for blk in w.planted[0]:
         assert blk in S
     assert np.max(np.abs(r["out"])) < 0.5   # bf16 half-ulp stays below 2e-3 there
+
+
+def test_boundary_values_bruteforce():
+    pins.check_boundary_bruteforce(O)

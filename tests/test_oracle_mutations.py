@@ -107,3 +107,23 @@ def test_position_off_by_one_caught(monkeypatch):
     monkeypatch.setattr(O, "query_position", lambda L, q_len, t, mb: min(int(L), mb * 128) - q_len + t - 1)
     w = make_workload("causal", 23, [1500, 130], 4, 16, 2, 4, KV_NVFP4, IDX_FP8, table="permute")
     _fails(pins.check_causal_positions, O, w)
+
+
+def test_boundary_off_by_one_caught(monkeypatch):
+    def bad(P, top_k, keep_last=True):
+        n = P.shape[0]
+        if n <= top_k + 1:
+            return None, None
+        Pk = P.astype(np.float64).copy()
+        if keep_last:
+            Pk[n - 1] = np.inf
+        order = np.lexsort((np.arange(n), -Pk))
+        return float(Pk[order[top_k]]), float(Pk[order[top_k + 1]])
+    monkeypatch.setattr(O, "boundary_values", bad)
+    _fails(pins.check_boundary_bruteforce, O)
+
+
+def test_boundary_ignoring_keep_last_caught(monkeypatch):
+    good = O.boundary_values
+    monkeypatch.setattr(O, "boundary_values", lambda P, k, keep_last=True: good(P, k, False))
+    _fails(pins.check_boundary_bruteforce, O)

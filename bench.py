@@ -5,24 +5,30 @@
 A step is one decode layer over one batch of the chosen synthetic
 configuration, inputs resident in HBM: one call of msa_decode_layer_single
 (one kernel: indexer + per-block max pool, then top-16 selection + sparse
-attention per item) where that path applies and runs the same arithmetic as
-the two-kernel path (--layer auto), else of msa_decode_layer (kernel 1:
-indexer + pool; kernel 2: selection + attention). Consecutive steps rotate
-over R device replicas of the inputs so that no step finds its bytes in the
-256 MB Infinity Cache. The K timed steps lie between two HIP events on the
-launch stream. A second pass over the same K steps has every kernel's
-dispatch record its own start and end events (hipExtLaunchKernel), which
-give the per-kernel durations.
+attention) where that path applies (--layer auto), else of msa_decode_layer
+(kernel 1: indexer + pool; kernel 2: selection + attention). Consecutive
+steps rotate over R device replicas of the inputs so that no step finds its
+bytes in the 256 MB Infinity Cache. W untimed steps, then K timed steps
+between two HIP events on the launch stream. After the timed region the same
+K steps run again with every kernel's dispatch recording its own start and
+end events (hipExtLaunchKernel): the per-kernel durations of the two-kernel
+path.
 Prints one JSON line on stdout (details on stderr):
 
   value        decode tokens/s per layer = B * T_q / step time
-  roofline     the dominant kernel (the single-launch layer kernel, or the
-               indexer scan of the two-kernel path): algorithmic bytes per
-               launch / its average duration, against the 8 TB/s HBM peak;
-               traffic = HBM bytes per launch from rocprofv3 counters, when a
-               record for the current kernel source exists (else null)
+  roofline     the dominant kernel: the single-launch layer kernel (its time
+               per launch is the timed region's time per step) or the
+               indexer scan of the two-kernel path (from the traced pass):
+               algorithmic bytes per launch / its average duration, against
+               the 8 TB/s HBM peak; traffic = HBM bytes per launch from
+               rocprofv3 counters, when a record for the current kernel
+               source exists (else null)
+  step         the step's algorithmic bytes term by term, rate and fraction
   cpu_baseline the float64 oracle on a bounded sample of the same workload,
-               timed on this host's cores
+               timed on this host's cores, and its comparison with the GPU
+  other_workloads  (default run) the 32K, 512K and ragged decode workloads:
+               step time, rate, fraction, and every query token's selection
+               checked against the oracle
 """
 import argparse
 import hashlib
@@ -66,34 +72,66 @@ def source_sha(names):
 
 
 # ------------------------------------------------------------ byte models
+#
+# Algorithmic bytes of one decode step: what the path has to read and write
+# at least once, nothing it re-reads, over-fetches or keeps as intermediates
+# (pooled scores, selections, partial softmax states are not counted).
 
-def indexer_bytes(w):
-    """Algorithmic bytes of the indexer + pool launch: every visible indexer
-    key (64 B codes + 4 B scale for FP8, 32 B codes + 4 B scales for NVFP4,
-    128 B for bf16), indexer queries and
-    weights, block-table entries read, pooled scores written."""
-    prm = w.params
-    B, Tq, Hi, maxb = prm["num_seqs"], prm["q_len"], prm["idx_heads"], prm["max_blocks_per_seq"]
-    L = np.minimum(w.ctx_lens.astype(np.int64), maxb * 128)
+IDX_KEY_BYTES = {0: 128, 1: 68, 2: 36}   # per token: bf16 row; FP8 row + fp32 scale; NVFP4 codes + 4 E4M3
+KV_BYTES = {0: 512, 1: 144}              # per token and KV head, K + V: bf16; NVFP4 codes + E4M3 scales
+
+
+def step_byte_terms(params, ctx_lens, union_blocks):
+    """Algorithmic bytes of one step, term by term. ctx_lens: int array [B];
+    union_blocks: the number of distinct blocks selected per sequence (the
+    union over its query tokens), summed over the batch. Terms:
+      idx_keys    every visible indexer key (codes + scales)
+      kv          K and V of the union of the selected blocks per sequence,
+                  for every KV head (codes + scales)
+      q, out      bf16 attention queries and outputs
+      idx_q, idx_w  bf16 indexer queries, fp32 head weights
+      table       the block-table entries of every visible block
+      ctx_lens    one int32 per sequence"""
+    B, Tq = int(params["num_seqs"]), int(params["q_len"])
+    Hq, G, Hi = int(params["num_q_heads"]), int(params["num_kv_heads"]), int(params["idx_heads"])
+    L = np.minimum(np.asarray(ctx_lens, dtype=np.int64), int(params["max_blocks_per_seq"]) * 128)
     nblk = (L + 127) // 128
-    per_tok = {0: 128, 1: 68, 2: 36}[int(prm["idx_dtype"])]  # bf16, FP8 (+fp32 scale), NVFP4 (+4 E4M3)
-    return int(L.sum() * per_tok + B * Tq * Hi * (64 * 2 + 4) + nblk.sum() * 4 + Tq * nblk.sum() * 4)
+    return {
+        "idx_keys": int(L.sum()) * IDX_KEY_BYTES[int(params["idx_dtype"])],
+        "kv": int(union_blocks) * G * 128 * KV_BYTES[int(params["kv_dtype"])],
+        "q": B * Tq * Hq * 128 * 2,
+        "out": B * Tq * Hq * 128 * 2,
+        "idx_q": B * Tq * Hi * 64 * 2,
+        "idx_w": B * Tq * Hi * 4,
+        "table": int(nblk.sum()) * 4,
+        "ctx_lens": B * 4,
+    }
 
 
-def attention_bytes(w, sel):
-    """Algorithmic bytes of the selection + attention launch: K+V of the
-    union of the selected blocks per (sequence, KV head) -- 144 B per token
-    per KV head for NVFP4 (codes + scales of K and V), 512 B for bf16 -- plus
-    queries, pooled scores read, selections and bf16 outputs."""
-    prm = w.params
-    B, Tq, Hq, G = prm["num_seqs"], prm["q_len"], prm["num_q_heads"], prm["num_kv_heads"]
-    per_tok = 144 if prm["kv_dtype"] == 1 else 512
-    blocks = 0
-    for b in range(B):
-        blocks += len(set(int(x) for x in sel[b].ravel() if x >= 0))
-    L = np.minimum(w.ctx_lens.astype(np.int64), prm["max_blocks_per_seq"] * 128)
-    pooled = int(((L + 127) // 128).sum()) * Tq * 4
-    return int(blocks * G * 128 * per_tok + B * Tq * Hq * 128 * 2 * 2 + B * Tq * prm["top_k"] * 4 + pooled)
+def union_blocks(sel):
+    """Distinct selected blocks per sequence, summed: sel int [B][Tq][top_k],
+    -1 padded."""
+    return sum(len(set(int(x) for x in sel[b].ravel() if x >= 0)) for b in range(sel.shape[0]))
+
+
+def indexer_bytes(params, ctx_lens):
+    """Bytes of the indexer + pool stage: indexer keys, indexer queries and
+    weights, block-table entries, context lengths."""
+    t = step_byte_terms(params, ctx_lens, 0)
+    return t["idx_keys"] + t["idx_q"] + t["idx_w"] + t["table"] + t["ctx_lens"]
+
+
+def attention_bytes(params, ctx_lens, sel):
+    """Bytes of the selection + attention stage: K/V of the union of the
+    selected blocks per sequence, queries and outputs."""
+    t = step_byte_terms(params, ctx_lens, union_blocks(sel))
+    return t["kv"] + t["q"] + t["out"]
+
+
+def dense_kv_bytes(params, ctx_lens):
+    """K/V bytes that dense attention over every visible key would read."""
+    L = np.minimum(np.asarray(ctx_lens, dtype=np.int64), int(params["max_blocks_per_seq"]) * 128)
+    return int(L.sum()) * int(params["num_kv_heads"]) * KV_BYTES[int(params["kv_dtype"])]
 
 
 def _records():
@@ -155,7 +193,56 @@ def write_traffic_record(fetch_csv, write_csv, kernel, config_id):
     print(json.dumps(rec))
 
 
-# ------------------------------------------------------------ cpu baseline
+# ------------------------------------------------------------ oracle checks
+
+TIE_REL = 1e-4   # selections may differ only where the k-th ranked pooled score is this close
+
+
+def selection_verdict(gpu_row, r, top_k, keep_last):
+    """0: the GPU selected the oracle's blocks; 1: the two sets differ only
+    in blocks whose oracle pooled score lies within TIE_REL (relative) of
+    the k-th ranked (keep-last adjusted) oracle pooled score; 2: otherwise."""
+    from oracle import msa_oracle as O
+    g = sorted(int(x) for x in gpu_row if x >= 0)
+    o = [int(x) for x in r["sel"]]
+    if g == o:
+        return 0
+    kth, _ = O.boundary_values(r["pooled"], top_k, keep_last)
+    if kth is None or not np.isfinite(kth) or len(g) != len(o):
+        return 2
+    for blk in set(g) ^ set(o):
+        if blk >= len(r["pooled"]) or abs(r["pooled"][blk] - kth) > TIE_REL * max(abs(kth), 1e-30):
+            return 2
+    return 1
+
+
+def compare_tokens(w, b, res, gpu_res, acc):
+    """Accumulate the comparison of sequence b's oracle results `res` with the
+    GPU step's selections and outputs into the dict `acc`."""
+    prm = w.params
+    for t, r in enumerate(res):
+        if r["p"] < 0:
+            continue
+        v = selection_verdict(gpu_res["sel"][b, t], r, prm["top_k"], prm["keep_last"])
+        acc["tokens"] += 1
+        acc["tie_band_tokens"] += v == 1
+        acc["other_selection_tokens"] += v == 2
+        if v == 0 and "out" in gpu_res:
+            err = np.abs(gpu_res["out"][b, t] - r["out"])
+            acc["max_abs"] = max(acc["max_abs"], float(err.max()))
+            acc["sum_abs"] += float(err.sum())
+            acc["n_elems"] += err.size
+
+
+def new_acc():
+    return dict(tokens=0, tie_band_tokens=0, other_selection_tokens=0, max_abs=0.0, sum_abs=0.0, n_elems=0)
+
+
+def acc_summary(acc):
+    return {"tokens_compared": acc["tokens"], "tie_band_tokens": acc["tie_band_tokens"],
+            "other_selection_tokens": acc["other_selection_tokens"], "out_max_abs": acc["max_abs"],
+            "out_mean_abs": acc["sum_abs"] / max(acc["n_elems"], 1)}
+
 
 def cpu_baseline(w, gpu_res, budget_s=20.0):
     """Time the oracle (as it stands) on whole sequences of the workload until
@@ -164,34 +251,166 @@ def cpu_baseline(w, gpu_res, budget_s=20.0):
     from oracle import msa_oracle as O
     try:
         from threadpoolctl import threadpool_info
-        threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+        blas = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
     except Exception:
-        threads = 1
+        blas = None
     prm = w.params
+    acc = new_acc()
     t0 = time.perf_counter()
-    done_tok, seqs, other_sel, max_err = 0, [], 0, 0.0
+    done_tok, seqs = 0, 0
     for b in range(prm["num_seqs"]):
         res = O.decode_sequence(w, b)
         done_tok += len(res)
-        seqs.append(b)
-        for t, r in enumerate(res):
-            if r["p"] < 0:
-                continue
-            g = sorted(int(x) for x in gpu_res["sel"][b, t] if x >= 0)
-            if g != list(r["sel"]):
-                other_sel += 1
-            else:
-                err = np.abs(gpu_res["out"][b, t] - r["out"])
-                small = np.abs(r["out"]) < 0.5
-                if small.any():
-                    max_err = max(max_err, float(err[small].max()))
+        seqs += 1
+        compare_tokens(w, b, res, gpu_res, acc)
         if time.perf_counter() - t0 > budget_s:
             break
     dt = time.perf_counter() - t0
-    return {"value": done_tok / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": "%d of %d sequences (%d query tokens), float64 numpy, %.1f s" % (
-                len(seqs), prm["num_seqs"], done_tok, dt),
-            "sample_check": {"tokens_with_other_selection": other_sel, "max_abs_where_o_below_0.5": max_err}}
+    return {"value": done_tok / dt, "unit": "tokens/s", "cores": len(os.sched_getaffinity(0)),
+            "blas_threads": blas, "kind": "oracle",
+            "sample": "%d of %d sequences (%d query tokens) of the same workload, float64 numpy, %.1f s" % (
+                seqs, prm["num_seqs"], done_tok, dt),
+            "sample_check": acc_summary(acc)}
+
+
+# ------------------------------------------------------------ GPU runs
+
+class Runner:
+    """Device replicas of one workload and the prebuilt C arguments of its
+    decode-layer call, so that a timed step is one C-ABI call."""
+
+    def __init__(self, w, layer="auto", replicas=0):
+        import ctypes
+        import torch
+        import block_sparse_attention_kv_amd as msa
+        self.w, self.torch, self.msa = w, torch, msa
+        prm = w.params
+        B, Tq, Hq = prm["num_seqs"], prm["q_len"], prm["num_q_heads"]
+        step_guess = indexer_bytes(prm, w.ctx_lens) + B * prm["num_kv_heads"] * 64 * 128 * 144
+        self.R = replicas or max(2, min(4, int(math.ceil(3 * 256e6 / max(step_guess, 1)))))
+        dev = "cuda"
+        self.reps = [msa.to_device(w, dev) for _ in range(self.R)]
+        self.out = torch.empty((B, Tq, Hq, 128), dtype=torch.int16, device=dev)
+        self.lse = torch.empty((B, Tq, Hq), dtype=torch.float32, device=dev)
+        self.sel = torch.empty((B, Tq, prm["top_k"]), dtype=torch.int32, device=dev)
+        self.ws = msa.alloc_workspace(self.reps[0][0], dev)
+        L = self.L = msa.load()
+        stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        ws_bytes = self.ws.numel() * self.ws.element_size()
+        vp = lambda t: ctypes.c_void_p(t.data_ptr())
+        self.keep, self.call_args = [], []
+        for params, cache, qs in self.reps:
+            c = cache.c()
+            self.keep.append(c)
+            self.call_args.append([ctypes.byref(params), ctypes.byref(c), vp(qs["q"]), vp(qs["idx_q"]),
+                                   vp(qs["idx_w"]), vp(self.out), vp(self.lse), vp(self.sel), vp(self.ws),
+                                   ctypes.c_size_t(ws_bytes), stream])
+        self.items = B * Tq * prm["num_kv_heads"]
+        self.cus = torch.cuda.get_device_properties(0).multi_processor_count
+        single_ok = prm["kv_dtype"] == 1 and prm["idx_dtype"] in (1, 2) and Tq <= 4
+        if layer == "auto":
+            # the single launch wins from two items per CU up, and wherever the
+            # scan is short enough that the gap between two kernels weighs more
+            # than 4 instead of 8 waves per item
+            self.single = single_ok and (self.items >= 2 * self.cus or
+                                         indexer_bytes(prm, w.ctx_lens) <= SINGLE_SCAN_BYTES)
+        else:
+            self.single = layer == "single"
+            if self.single and not single_ok:
+                raise SystemExit("--layer single: this configuration needs the two-kernel path")
+        self.kernel = "decode_layer_single" if self.single else "indexer_pool"
+        self.entry = "msa_decode_layer_single" if self.single else "msa_decode_layer"
+        self.plain = L.msa_decode_layer_single if self.single else L.msa_decode_layer
+        self.traced_fn = L.msa_decode_layer_single_traced if self.single else L.msa_decode_layer_traced
+        self.stage_names = ["decode_layer_single"] if self.single else list(msa.STAGE_NAMES)
+        torch.cuda.synchronize()
+
+    def step(self, i, events=None):
+        st = self.plain(*self.call_args[i % self.R]) if events is None else \
+            self.traced_fn(*self.call_args[i % self.R], events)
+        if st != 0:
+            raise RuntimeError("%s: %s" % (self.entry, self.L.msa_last_error().decode()))
+
+    def results(self):
+        torch = self.torch
+        torch.cuda.synchronize()
+        return {"sel": self.sel.cpu().numpy(),
+                "out": (self.out.view(torch.int16).cpu().numpy().astype(np.uint16).astype(np.uint32) << 16)
+                .view(np.float32).astype(np.float64)}
+
+    def timed(self, steps):
+        """K steps between two HIP events on the launch stream: ms per step."""
+        torch = self.torch
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for i in range(steps):
+            self.step(i)
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / steps
+
+    def traced(self, steps):
+        """K steps whose kernels record their own start and end events
+        (hipExtLaunchKernel): per-kernel durations (ms) of every step."""
+        import ctypes
+        torch = self.torch
+        n = len(self.stage_names)
+        kev = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * n)] for _ in range(steps)]
+        for row in kev:          # create the HIP events before the pass
+            for e in row:
+                e.record()
+        torch.cuda.synchronize()
+        arrays = [(ctypes.c_void_p * (2 * n))(*[e.cuda_event for e in row]) for row in kev]
+        for i in range(steps):
+            self.step(i, arrays[i])
+        torch.cuda.synchronize()
+        return [np.array([kev[i][2 * s].elapsed_time(kev[i][2 * s + 1]) for i in range(steps)]) for s in range(n)]
+
+    def release(self):
+        self.reps = self.call_args = self.keep = None
+        self.out = self.lse = self.sel = self.ws = None
+        self.torch.cuda.synchronize()
+        self.torch.cuda.empty_cache()
+
+
+def step_report(w, ms_step, sel):
+    prm = w.params
+    terms = step_byte_terms(prm, w.ctx_lens, union_blocks(sel))
+    step_b = sum(terms.values())
+    gbps = step_b / (ms_step * 1e-3) / 1e9
+    return terms, step_b, gbps
+
+
+def other_workload(cfg, steps, warmup, layer):
+    """Compact measurement of another decode workload: step time, rate,
+    fraction of the HBM peak, and the selection of every query token checked
+    against the oracle (tie-band and other differences counted)."""
+    from oracle import msa_oracle as O
+    from workloads import make_config, CONFIG_NAMES
+    t0 = time.perf_counter()
+    w = make_config(cfg)
+    run = Runner(w, layer)
+    for i in range(warmup):
+        run.step(i)
+    ms = run.timed(steps)
+    gpu_res = run.results()
+    entry = run.entry
+    run.release()
+    terms, step_b, gbps = step_report(w, ms, gpu_res["sel"])
+    acc = new_acc()
+    for b in range(w.B):
+        compare_tokens(w, b, O.decode_sequence(w, b), gpu_res, acc)
+    prm = w.params
+    rep = {"config_id": str(cfg), "workload": CONFIG_NAMES[cfg], "entry": entry, "steps": steps,
+           "warmup": warmup, "ms_per_step": ms, "tokens_per_s": prm["num_seqs"] * prm["q_len"] / (ms * 1e-3),
+           "algorithmic_bytes": step_b, "gbps": gbps, "frac": gbps / HBM_PEAK_GBPS,
+           "oracle_check": acc_summary(acc)}
+    log("%s: %s %.4f ms/step, %.0f GB/s (%.3f), ties %d, other %d (%.1f s)" % (
+        w.name, entry, ms, gbps, gbps / HBM_PEAK_GBPS, acc["tie_band_tokens"], acc["other_selection_tokens"],
+        time.perf_counter() - t0))
+    del w
+    return rep
 
 
 # ------------------------------------------------------------------ main
@@ -207,6 +426,9 @@ def main():
     ap.add_argument("--replicas", type=int, default=0, help="input copies rotated per step (0: auto)")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-others", action="store_true",
+                    help="skip the compact measurements of the other decode workloads")
+    ap.add_argument("--other-steps", type=int, default=50)
     ap.add_argument("--profile-steps", type=int, default=0,
                     help="only run this many steps and a 1 GiB calibration copy (for rocprofv3 runs)")
     ap.add_argument("--layer", choices=("auto", "single", "two"), default="auto",
@@ -237,68 +459,17 @@ def main():
     w = make_config(args.config, idx_dtype=IDX_NVFP4 if args.idx_dtype == "nvfp4" else None)
     log("generated %s in %.1f s (%.2f GB host)" % (w.name, time.perf_counter() - t0, w.nbytes() / 1e9))
     prm = w.params
-    B, Tq, Hq = prm["num_seqs"], prm["q_len"], prm["num_q_heads"]
-    step_guess = indexer_bytes(w) + B * prm["num_kv_heads"] * 64 * 128 * 144
-    R = args.replicas or max(2, min(4, int(math.ceil(3 * 256e6 / max(step_guess, 1)))))
-    dev = "cuda"
-    reps = [msa.to_device(w, dev) for _ in range(R)]
-    torch.cuda.synchronize()
-    log("uploaded %d replica(s) in %.1f s" % (R, time.perf_counter() - t0))
-    out = torch.empty((B, Tq, Hq, 128), dtype=torch.int16, device=dev)
-    lse = torch.empty((B, Tq, Hq), dtype=torch.float32, device=dev)
-    sel = torch.empty((B, Tq, prm["top_k"]), dtype=torch.int32, device=dev)
-    ws = msa.alloc_workspace(reps[0][0], dev)
-
-    # Every C argument is built once, so that a timed step is one C-ABI call:
-    # the host then stays ahead of the GPU and the queue never drains.
-    import ctypes
-    L = msa.load()
-    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-    ws_bytes = ws.numel() * ws.element_size()
-    keep = []
-
-    def vp(t):
-        return ctypes.c_void_p(t.data_ptr())
-
-    call_args = []
-    for params, cache, qs in reps:
-        c = cache.c()
-        keep.append(c)
-        call_args.append([ctypes.byref(params), ctypes.byref(c), vp(qs["q"]), vp(qs["idx_q"]), vp(qs["idx_w"]),
-                          vp(out), vp(lse), vp(sel), vp(ws), ctypes.c_size_t(ws_bytes), stream])
-
-    items = B * Tq * prm["num_kv_heads"]
-    cus = torch.cuda.get_device_properties(0).multi_processor_count
-    single_ok = prm["kv_dtype"] == 1 and prm["idx_dtype"] in (1, 2) and Tq <= 4
-    if args.layer == "auto":
-        # the single launch wins from two items per CU up, and wherever the
-        # scan is short enough that the gap between two kernels weighs more
-        # than 4 instead of 8 waves per item (measured: 32K x 8 sequences)
-        single = single_ok and (items >= 2 * cus or indexer_bytes(w) <= SINGLE_SCAN_BYTES)
-    else:
-        single = args.layer == "single"
-        if single and not single_ok:
-            raise SystemExit("--layer single: this configuration needs the two-kernel path")
-    kernel = "decode_layer_single" if single else "indexer_pool"
-    plain = L.msa_decode_layer_single if single else L.msa_decode_layer
-    traced = L.msa_decode_layer_single_traced if single else L.msa_decode_layer_traced
-    entry = "msa_decode_layer_single" if single else "msa_decode_layer"
-    log("layer path: %s (%d items, %d compute units)" % (entry, items, cus))
-
-    def step(i, events=None):
-        if events is None:
-            st = plain(*call_args[i % R])
-        else:
-            st = traced(*call_args[i % R], events)
-        if st != 0:
-            raise RuntimeError("%s: %s" % (entry, L.msa_last_error().decode()))
+    B, Tq = prm["num_seqs"], prm["q_len"]
+    run = Runner(w, args.layer, args.replicas)
+    log("uploaded %d replica(s) in %.1f s; layer path: %s (%d items, %d compute units)" % (
+        run.R, time.perf_counter() - t0, run.entry, run.items, run.cus))
 
     if args.profile_steps:
         for i in range(args.profile_steps):
-            step(i)
+            run.step(i)
         torch.cuda.synchronize()
         log("profile run: %d steps done" % args.profile_steps)
-        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
         dst.copy_(src)
         torch.cuda.synchronize()
@@ -306,57 +477,22 @@ def main():
         return
 
     for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    gpu_res = {"sel": sel.cpu().numpy(),
-               "out": (out.view(torch.int16).cpu().numpy().astype(np.uint16).astype(np.uint32) << 16)
-               .view(np.float32).astype(np.float64)}
-
+        run.step(i)
     # ---- timed region: K steps between two HIP events on the launch stream
-    torch.cuda.synchronize()
-    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    wall0 = time.perf_counter()
-    t_start.record()
-    for i in range(args.steps):
-        step(i)
-    t_end.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    ms_step = t_start.elapsed_time(t_end) / args.steps
-    log("timed %d steps: %.4f ms/step (events), %.4f ms/step (wall)" % (args.steps, ms_step,
-                                                                       wall * 1e3 / args.steps))
+    ms_step = run.timed(args.steps)
+    gpu_res = run.results()
+    log("timed %d steps: %.4f ms/step" % (args.steps, ms_step))
 
-    # ---- per-kernel durations: the same K steps again, each kernel's dispatch
-    # recording its own start and end event (hipExtLaunchKernel); the events
-    # lengthen the step a little, so the step time above comes from the
-    # uninstrumented pass
-    n_st = 1 if single else msa.NUM_STAGES
-    stage_names = ["decode_layer_single"] if single else list(msa.STAGE_NAMES)
-    kev = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * n_st)] for _ in range(args.steps)]
-    for row in kev:          # create the HIP events before the timed pass
-        for e in row:
-            e.record()
-    torch.cuda.synchronize()
-    ev_arrays = [(ctypes.c_void_p * (2 * n_st))(*[e.cuda_event for e in row]) for row in kev]
-    k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    k0.record()
-    for i in range(args.steps):
-        step(i, ev_arrays[i])
-    k1.record()
-    torch.cuda.synchronize()
-    ms_step_traced = k0.elapsed_time(k1) / args.steps
-    stage_all = [np.array([kev[i][2 * s].elapsed_time(kev[i][2 * s + 1]) for i in range(args.steps)])
-                 for s in range(n_st)]
+    # ---- per-kernel durations: the same K steps again, each kernel's
+    # dispatch recording its own start and end (these events lengthen the
+    # step a little, so the step time above comes from the plain pass)
+    stage_all = run.traced(args.steps)
     stage_ms = [float(np.mean(d)) for d in stage_all]
-    # spread of the per-step kernel durations (ms): p10, median, p90
-    stage_pct = {n: [float(x) for x in np.percentile(d, [10, 50, 90])] for n, d in zip(stage_names, stage_all)}
-    log("kernels (ms): " + ", ".join("%s %.4f" % (n, v) for n, v in zip(stage_names, stage_ms)) +
-        "; step with kernel events %.4f ms" % ms_step_traced)
-    log("kernel durations p10 / median / p90 (ms): " +
-        ", ".join("%s %.4f / %.4f / %.4f" % (n, *stage_pct[n]) for n in stage_names))
+    stage_pct = {n: [float(x) for x in np.percentile(d, [10, 50, 90])] for n, d in zip(run.stage_names, stage_all)}
+    log("kernels (ms, event-traced pass): " + ", ".join("%s %.4f" % (n, v) for n, v in zip(run.stage_names, stage_ms)))
 
-    # ---- attainable copy bandwidth on this machine (context)
-    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    # ---- attainable bandwidth on this machine (context)
+    src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
     dst = torch.empty_like(src)
     for _ in range(3):
         dst.copy_(src)
@@ -367,8 +503,7 @@ def main():
     c1.record()
     torch.cuda.synchronize()
     copy_gbps = 2 * (1 << 30) * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9
-    # ---- attainable read bandwidth: the library's streaming read kernel
-    chk = torch.zeros(4, dtype=torch.int32, device=dev)
+    chk = torch.zeros(4, dtype=torch.int32, device="cuda")
     for _ in range(3):
         msa.msa_debug_read_bandwidth(src, chk)
     c0.record()
@@ -380,23 +515,27 @@ def main():
     log("attainable on this box: read %.0f GB/s (1 GiB stream), device copy %.0f GB/s (read + write)"
         % (read_gbps, copy_gbps))
     del src, dst
+    kernel, entry, single, stage_names = run.kernel, run.entry, run.single, run.stage_names
+    run.release()
 
-    idx_b = indexer_bytes(w)
-    att_b = attention_bytes(w, gpu_res["sel"])
-    step_b = idx_b + att_b
-    step_gbps = step_b / (ms_step * 1e-3) / 1e9
-    if single:   # one kernel moves the step's bytes
-        kern_b, kern_ms = step_b, stage_ms[0]
-        stage_detail = {}
-    else:        # the indexer kernel dominates
+    terms, step_b, step_gbps = step_report(w, ms_step, gpu_res["sel"])
+    idx_b = indexer_bytes(prm, w.ctx_lens)
+    att_b = attention_bytes(prm, w.ctx_lens, gpu_res["sel"])
+    stages = {}
+    if single:
+        # one kernel is the whole step: its duration per launch is the timed
+        # region's time per step (back-to-back launches on one stream)
+        kern_b, kern_ms = step_b, ms_step
+    else:
         kern_b, kern_ms = idx_b, stage_ms[0]
-        stage_detail = {"attention_gbps": att_b / (stage_ms[1] * 1e-3) / 1e9}
+        for n, b_, ms in zip(stage_names, (idx_b, att_b), stage_ms):
+            stages[n] = {"algorithmic_bytes": b_, "avg_ms": ms, "gbps": b_ / (ms * 1e-3) / 1e9,
+                         "frac": b_ / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS}
     kern_gbps = kern_b / (kern_ms * 1e-3) / 1e9
     rec = traffic_record(kernel, wkey)
-    tokens = B * Tq
     res = {
         "metric": METRIC,
-        "value": tokens / (ms_step * 1e-3),
+        "value": B * Tq / (ms_step * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -410,22 +549,28 @@ def main():
         "config": {"workload": CONFIG_NAMES[args.config] + ("" if args.idx_dtype == "fp8" else
                                                              ", NVFP4 idx keys instead of FP8"),
                    "config_id": wkey, "batch": B, "q_len": Tq,
-                   "ctx_len": int(w.ctx_lens.max()), "q_heads": Hq, "kv_heads": prm["num_kv_heads"],
-                   "idx_heads": prm["idx_heads"], "top_k": prm["top_k"], "block": 128,
-                   "input_replicas": R},
+                   "ctx_len": int(w.ctx_lens.max()), "q_heads": prm["num_q_heads"],
+                   "kv_heads": prm["num_kv_heads"], "idx_heads": prm["idx_heads"], "top_k": prm["top_k"],
+                   "block": 128, "input_replicas": run.R},
         "roofline": {"bound": "hbm", "kernel": kernel, "achieved": kern_gbps, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": kern_gbps / HBM_PEAK_GBPS,
                      "traffic": None if rec is None else rec["traffic_bytes_per_launch"],
-                     "algorithmic_bytes": kern_b, "avg_ms": kern_ms},
-        "step": dict({"entry": entry, "algorithmic_bytes": step_b, "gbps": step_gbps,
-                      "frac": step_gbps / HBM_PEAK_GBPS, "stage_ms": dict(zip(stage_names, stage_ms)),
-                      "stage_ms_p10_p50_p90": stage_pct,
-                      "ms_per_step_with_kernel_events": ms_step_traced, "indexer_bytes": idx_b,
-                      "attention_bytes": att_b, "copy_gbps_attainable": copy_gbps,
-                      "read_gbps_attainable": read_gbps}, **stage_detail),
+                     "algorithmic_bytes": kern_b, "avg_ms": kern_ms,
+                     "avg_ms_from": "timed region, one kernel per step" if single else "event-traced pass"},
+        "step": {"entry": entry, "algorithmic_bytes": step_b, "byte_terms": terms, "gbps": step_gbps,
+                 "frac": step_gbps / HBM_PEAK_GBPS, "dense_kv_bytes": dense_kv_bytes(prm, w.ctx_lens),
+                 "msa_over_dense": (terms["idx_keys"] + terms["kv"]) / dense_kv_bytes(prm, w.ctx_lens),
+                 "traced_stage_ms": dict(zip(stage_names, stage_ms)),
+                 "traced_stage_ms_p10_p50_p90": stage_pct, "stages": stages,
+                 "indexer_bytes": idx_b, "attention_bytes": att_b,
+                 "copy_gbps_attainable": copy_gbps, "read_gbps_attainable": read_gbps},
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, gpu_res, args.cpu_budget)
+    del w
+    if not args.no_others and args.config == 3 and args.idx_dtype == "fp8":
+        res["other_workloads"] = [other_workload(c, args.other_steps, max(args.warmup, 5), args.layer)
+                                  for c in (2, 4, 5)]
     print(json.dumps(res), flush=True)
 
 

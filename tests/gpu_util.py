@@ -10,16 +10,23 @@ host workload and compare with the oracle. Tolerances (stated once here):
                       (relative) of the k-th ranked pooled score; such tokens
                       are counted and reported
   attention output    against the oracle under the GPU's own selection
-                      (fp32 accumulate, bf16 output). Element by element
-                      |gpu - o| <= max(2e-3, 1 bf16 ulp of o): that is
-                      max-abs 2e-3 wherever |o| < 0.5 -- where bf16 can hold
-                      that accuracy (its ulp there is <= 1.95e-3) -- and one
-                      ulp of the output format above (a few keys, or the x8
-                      outlier channels, give |o| >= 1, where bf16 rounding by
-                      itself exceeds 2e-3). Mean-abs <= 2e-4 over all
-                      elements, against the unrounded oracle when strict,
-                      else against the oracle rounded to bf16 (short
-                      contexts, where the outputs are O(1)).
+                      (fp32 accumulate, bf16 output), element by element:
+                      |o| < 0.5:  |gpu - o| <= 2e-3
+                      |o| >= 0.5: |gpu - o| <= ulp(o)/2 + slack, where ulp
+                      is bf16's at |o| (ulp/2 >= 1.95e-3 there: the output
+                      format alone cannot hold 2e-3) and slack is the
+                      first-order effect of the one rounding the kernel adds
+                      before the output: the softmax weights p_j are rounded
+                      to the matrix-core operand format (fp16 for NVFP4 K/V,
+                      relative error <= u = 2^-11; bf16 for a bf16 cache,
+                      u = 2^-9), which moves o_d by at most
+                      u * sum_j p_j |v_jd - o_d|, plus 2^-20 times that sum
+                      and |o| for the fp32 exp2, accumulation and division.
+                      Mean-abs <= 2e-4 over all elements, against the
+                      unrounded oracle when strict (the decode workloads,
+                      whose outputs are small), else against the oracle
+                      rounded to bf16 (short contexts, where outputs are O(1)
+                      and bf16 rounding alone exceeds 2e-4 on average).
   lse                 abs 2e-3
 """
 import math
@@ -137,17 +144,46 @@ def bf16_round(x):
     return u.astype(np.uint32).view(np.float32).astype(np.float64)
 
 
-def check_out(gpu, ref, label="", strict=False):
-    """Returns (max-abs over |o| < 0.5, max-abs overall, mean-abs)."""
+# unit roundoff of the softmax weights' operand format: fp16 (NVFP4 K/V), bf16 (bf16 K/V)
+P_ROUND = {1: 2.0 ** -11, 0: 2.0 ** -9}
+FP32_SLACK = 2.0 ** -20  # exp2, accumulation and the final division in fp32
+
+
+def attend_with_slack(w, b, t, blocks, p_t):
+    """The oracle's output under `blocks` plus the per-element slack of the
+    rounding of the softmax weights: u * sum_j p_j |v_jd - o_d| (u = P_ROUND
+    of the cache's K/V format, p_j = the oracle's softmax weights, v_j its
+    decoded values)."""
+    o, lse = O.attend_token(w, b, t, blocks, p_t)
+    prm = w.params
+    Hq, G = int(prm["num_q_heads"]), int(prm["num_kv_heads"])
+    grp = Hq // G
+    q = O.bf16_to_f64(w.q[b, t])
+    scale = O.softmax_scale(prm)
+    spread = np.zeros_like(o)
+    for g in range(G):
+        K, V = O.gather_selected(w, b, blocks, g, p_t)
+        if K.shape[0] == 0:
+            continue
+        hs = slice(g * grp, (g + 1) * grp)
+        p = np.exp(scale * (q[hs] @ K.T) - lse[hs, None])            # [grp][n]
+        spread[hs] = np.stack([p[i] @ np.abs(V - o[g * grp + i]) for i in range(grp)])
+    return o, lse, (P_ROUND[int(prm["kv_dtype"])] + FP32_SLACK) * spread + FP32_SLACK * np.abs(o)
+
+
+def check_out(gpu, ref, slack, label="", strict=False):
+    """Returns (max-abs over |o| < 0.5, max-abs overall, mean-abs). slack:
+    per-element slack where |o| >= 0.5 (attend_with_slack)."""
     gpu, ref = np.asarray(gpu).ravel(), np.asarray(ref).ravel()
+    slack = np.asarray(slack).ravel()
     err = np.abs(gpu - ref)
-    bound = np.maximum(OUT_MAX_ABS, bf16_ulp(ref))
+    big = np.abs(ref) >= 0.5
+    bound = np.where(big, 0.5 * bf16_ulp(ref) + slack, OUT_MAX_ABS)
     worst = int(np.argmax(err - bound))
-    assert np.all(err <= bound), (label, "beyond max(2e-3, 1 bf16 ulp)", float(err[worst]), float(ref[worst]),
-                                  float(gpu[worst]))
-    small = np.abs(ref) < 0.5
+    assert np.all(err <= bound), (label, "beyond the element bound", float(err[worst]), float(bound[worst]),
+                                  float(ref[worst]), float(gpu[worst]))
+    small = ~big
     mx_small = float(err[small].max()) if small.any() else 0.0
-    assert mx_small <= OUT_MAX_ABS, (label, "max-abs where |o| < 0.5", mx_small)
     if strict:
         assert err.mean() <= OUT_MEAN_ABS, (label, "mean-abs", float(err.mean()))
     else:
@@ -189,28 +225,75 @@ def indexer_parity(w, run=None):
     return ties
 
 
-def layer_parity(w, run=None, seqs=None, tokens=None, strict=False, single=False):
-    """Fused layer (the single-launch one when single) vs the oracle for the
-    listed sequences (default all). Returns (number of tie-band selection
-    differences, max-abs where |o| < 0.5, mean-abs)."""
-    run = run or Run(w)
-    res = run.layer(single=single)
+def oracle_outputs(w, sel, tokens=None):
+    """The oracle's outputs, lse and output slack (attend_with_slack) of every
+    (sequence, token) under the selection array sel [B][Tq][top_k]
+    (-1 padded)."""
     prm = w.params
-    ties, gots, refs = 0, [], []
-    for b in (range(prm["num_seqs"]) if seqs is None else seqs):
-        ref = O.decode_sequence(w, b, tokens=tokens)
-        for i, r in enumerate(ref):
-            t = i if tokens is None else tokens[i]
-            lab = "%s b=%d t=%d" % (w.name, b, t)
+    B, Tq, Hq = int(prm["num_seqs"]), int(prm["q_len"]), int(prm["num_q_heads"])
+    o = np.zeros((B, Tq, Hq, 128))
+    lse = np.full((B, Tq, Hq), -np.inf)
+    slack = np.zeros((B, Tq, Hq, 128))
+    for b in range(B):
+        for t in (range(Tq) if tokens is None else tokens):
+            p_t = O.query_position(w.ctx_lens[b], Tq, t, prm["max_blocks_per_seq"])
+            if p_t < 0:
+                continue
+            S = [int(x) for x in sel[b, t] if x >= 0]
+            o[b, t], lse[b, t], slack[b, t] = attend_with_slack(w, b, t, S, p_t)
+    return o, lse, slack
+
+
+def compare_layer(w, res, refs, seqs=None, strict=False, label=None):
+    """Compare one layer call's results `res` (Run.layer) with the oracle's
+    per-sequence results refs[b] (decode_sequence lists) for the sequences
+    `seqs` (default: all of refs). Returns (tie-band selection differences,
+    max-abs where |o| < 0.5, mean-abs)."""
+    prm = w.params
+    label = label or w.name
+    ties, gots, want, slacks = 0, [], [], []
+    for b in (sorted(refs) if seqs is None else seqs):
+        for r in refs[b]:
+            t = r["t"]
+            lab = "%s b=%d t=%d" % (label, b, t)
             if r["p"] < 0:
                 assert np.all(res["sel"][b, t] == -1), lab
                 assert np.all(res["out"][b, t] == 0), lab
                 continue
             ties += check_selection(res["sel"][b, t], r["pooled"], r["sel"], prm["top_k"], prm["keep_last"], lab)
             S = [int(x) for x in res["sel"][b, t] if x >= 0]
-            o, lse = O.attend_token(w, b, t, S, r["p"])
+            if S == [int(x) for x in r["sel"]]:
+                o, lse, sl = r["out"], r["lse"], r["slack"]
+            else:
+                o, lse, sl = attend_with_slack(w, b, t, S, r["p"])
             gots.append(res["out"][b, t].ravel())
-            refs.append(o.ravel())
+            want.append(o.ravel())
+            slacks.append(sl.ravel())
             check_lse(res["lse"][b, t], lse, lab)
-    mx, mx_all, mean = check_out(np.concatenate(gots), np.concatenate(refs), w.name, strict)
+    mx, mx_all, mean = check_out(np.concatenate(gots), np.concatenate(want), np.concatenate(slacks), label, strict)
     return ties, mx, mean
+
+
+def oracle_refs(w, seqs=None, tokens=None):
+    """decode_sequence of the listed sequences (default all), each token's
+    dict extended with its index t and the output slack under the oracle's
+    own selection."""
+    refs = {}
+    for b in (range(w.B) if seqs is None else seqs):
+        res = O.decode_sequence(w, b, tokens=tokens)
+        for i, r in enumerate(res):
+            r["t"] = i if tokens is None else tokens[i]
+            r["slack"] = np.zeros_like(r["out"])
+            if r["p"] >= 0:
+                _, _, r["slack"] = attend_with_slack(w, b, r["t"], [int(x) for x in r["sel"]], r["p"])
+        refs[b] = res
+    return refs
+
+
+def layer_parity(w, run=None, seqs=None, tokens=None, strict=False, single=False):
+    """Fused layer (the single-launch one when single) vs the oracle for the
+    listed sequences (default all). Returns (number of tie-band selection
+    differences, max-abs where |o| < 0.5, mean-abs)."""
+    run = run or Run(w)
+    res = run.layer(single=single)
+    return compare_layer(w, res, oracle_refs(w, seqs, tokens), strict=strict)

@@ -134,19 +134,6 @@ def test_single_workspace_holds_no_stale_scores():
             assert np.array_equal(g.view(np.uint8), x.view(np.uint8)), okey
 
 
-@pytest.mark.parametrize("cfg,idx", [(2, IDX_FP8), (3, IDX_FP8), (3, IDX_NVFP4), (4, IDX_FP8), (5, IDX_FP8)])
-def test_single_full_size(cfg, idx):
-    # the decode configurations at full size (32K x 8, the 128K speculative
-    # verify batch of 32 x 4 tokens with FP8 and NVFP4 indexer keys, 512K x 4,
-    # 64 ragged sequences); bit for bit against the two-kernel layer, plus the
-    # last sequence's last token against the oracle
-    w = make_config(cfg, idx_dtype=idx)
-    run = _same_as_two_kernel(w)
-    ties, mx, mean = G.layer_parity(w, run=run, seqs=[w.params["num_seqs"] - 1], tokens=[w.params["q_len"] - 1],
-                                    single=True)
-    print("config %d single: ties %d, out max-abs %.2e mean-abs %.2e" % (cfg, ties, mx, mean))
-
-
 def test_single_rejects_unsupported():
     w = make_workload("single_bf16", 66, [300], 4, 16, 2, 4, KV_BF16, IDX_BF16, table="permute")
     run = G.Run(w)

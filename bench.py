@@ -5,14 +5,18 @@
 A step is one decode layer over one batch of the chosen synthetic
 configuration, inputs resident in HBM: one call of msa_decode_layer_single
 (one kernel: indexer + per-block max pool, then top-16 selection + sparse
-attention) where that path applies (--layer auto), else of msa_decode_layer
-(kernel 1: indexer + pool; kernel 2: selection + attention). Consecutive
+attention) where that path applies (--layer auto: NVFP4 K/V, FP8 or NVFP4
+indexer keys, q_len <= 4), else of msa_decode_layer (kernel 1: indexer +
+pool; kernel 2: selection + attention). Consecutive
 steps rotate over R device replicas of the inputs so that no step finds its
-bytes in the 256 MB Infinity Cache. W untimed steps, then K timed steps
-between two HIP events on the launch stream. After the timed region the same
-K steps run again with every kernel's dispatch recording its own start and
-end events (hipExtLaunchKernel): the per-kernel durations of the two-kernel
-path.
+bytes in the 256 MB Infinity Cache. Order: the device's attainable read and
+copy bandwidth (about 30 ms of streaming), W untimed steps, K steps whose
+kernels' dispatches record their own start and end events
+(hipExtLaunchKernel: the per-kernel durations of the two-kernel path), then
+the timed region: K steps between two HIP events on the launch stream. The
+GPU's clocks settle only after some milliseconds of load (a 50-step run
+right after start ran about 5% slower than later ones), so the measurements
+before the timed region also serve to bring it to its steady state.
 Prints one JSON line on stdout (details on stderr):
 
   value        decode tokens/s per layer = B * T_q / step time
@@ -45,9 +49,6 @@ METRIC = "MSA decode tokens/s per layer at 128K ctx; achieved HBM GB/s vs 8 TB/s
 ROOT = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(ROOT, "block_sparse_attention_kv_amd", "csrc")
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "traffic.json")
-# --layer auto: indexer bytes per step up to which the single launch is
-# taken whatever the number of attention items
-SINGLE_SCAN_BYTES = 64e6
 # the files each kernel's device code is compiled from (a traffic record is
 # valid only for the sources it was taken on)
 KERNELS = {
@@ -309,11 +310,9 @@ class Runner:
         self.cus = torch.cuda.get_device_properties(0).multi_processor_count
         single_ok = prm["kv_dtype"] == 1 and prm["idx_dtype"] in (1, 2) and Tq <= 4
         if layer == "auto":
-            # the single launch wins from two items per CU up, and wherever the
-            # scan is short enough that the gap between two kernels weighs more
-            # than 4 instead of 8 waves per item
-            self.single = single_ok and (self.items >= 2 * self.cus or
-                                         indexer_bytes(prm, w.ctx_lens) <= SINGLE_SCAN_BYTES)
+            # the single launch wherever it applies: it matches or beats the
+            # two-kernel layer on every measured workload
+            self.single = single_ok
         else:
             self.single = layer == "single"
             if self.single and not single_ok:
@@ -433,8 +432,9 @@ def main():
                     help="only run this many steps and a 1 GiB calibration copy (for rocprofv3 runs)")
     ap.add_argument("--layer", choices=("auto", "single", "two"), default="auto",
                     help="single: msa_decode_layer_single; two: msa_decode_layer; auto: single where it applies "
-                         "and has at least two (sequence, token, KV head) items per compute unit or a short "
-                         "indexer scan (<= 64 MB)")
+                         "(NVFP4 K/V, FP8 or NVFP4 indexer keys, q_len <= 4)")
+    ap.add_argument("--layer-splits", type=int, default=0, choices=(0, 1, 2, 4),
+                    help="workgroups per attention item of the single launch (0: the library's choice)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write a record of profiles/traffic.json from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE "
                          "counter collections of a --profile-steps run, and exit")
@@ -455,6 +455,8 @@ def main():
     import block_sparse_attention_kv_amd as msa
     from workloads import make_config, CONFIG_NAMES, IDX_NVFP4
 
+    if args.layer_splits:
+        msa.msa_debug_layer_splits(args.layer_splits)
     t0 = time.perf_counter()
     w = make_config(args.config, idx_dtype=IDX_NVFP4 if args.idx_dtype == "nvfp4" else None)
     log("generated %s in %.1f s (%.2f GB host)" % (w.name, time.perf_counter() - t0, w.nbytes() / 1e9))
@@ -476,22 +478,10 @@ def main():
         log("calibration copy: 1 GiB read + 1 GiB written")
         return
 
-    for i in range(args.warmup):
-        run.step(i)
-    # ---- timed region: K steps between two HIP events on the launch stream
-    ms_step = run.timed(args.steps)
-    gpu_res = run.results()
-    log("timed %d steps: %.4f ms/step" % (args.steps, ms_step))
-
-    # ---- per-kernel durations: the same K steps again, each kernel's
-    # dispatch recording its own start and end (these events lengthen the
-    # step a little, so the step time above comes from the plain pass)
-    stage_all = run.traced(args.steps)
-    stage_ms = [float(np.mean(d)) for d in stage_all]
-    stage_pct = {n: [float(x) for x in np.percentile(d, [10, 50, 90])] for n, d in zip(run.stage_names, stage_all)}
-    log("kernels (ms, event-traced pass): " + ", ".join("%s %.4f" % (n, v) for n, v in zip(run.stage_names, stage_ms)))
-
-    # ---- attainable bandwidth on this machine (context)
+    # ---- attainable bandwidth on this machine (context), measured first: the
+    # GPU's clocks settle only after some milliseconds of load, and this
+    # measurement and the event-traced pass below provide that load before
+    # the timed region
     src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
     dst = torch.empty_like(src)
     for _ in range(3):
@@ -507,14 +497,30 @@ def main():
     for _ in range(3):
         msa.msa_debug_read_bandwidth(src, chk)
     c0.record()
-    for _ in range(10):
+    for _ in range(30):
         msa.msa_debug_read_bandwidth(src, chk)
     c1.record()
     torch.cuda.synchronize()
-    read_gbps = (1 << 30) * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    read_gbps = (1 << 30) * 30 / (c0.elapsed_time(c1) * 1e-3) / 1e9
     log("attainable on this box: read %.0f GB/s (1 GiB stream), device copy %.0f GB/s (read + write)"
         % (read_gbps, copy_gbps))
     del src, dst
+
+    for i in range(args.warmup):
+        run.step(i)
+    # ---- per-kernel durations: K steps whose kernels' dispatches record
+    # their own start and end (these events lengthen the step a little, so
+    # the step time comes from the plain pass below)
+    stage_all = run.traced(args.steps)
+    stage_ms = [float(np.mean(d)) for d in stage_all]
+    stage_pct = {n: [float(x) for x in np.percentile(d, [10, 50, 90])] for n, d in zip(run.stage_names, stage_all)}
+    log("kernels (ms, event-traced pass): " + ", ".join("%s %.4f" % (n, v) for n, v in zip(run.stage_names, stage_ms)))
+
+    # ---- timed region: K steps between two HIP events on the launch stream
+    ms_step = run.timed(args.steps)
+    gpu_res = run.results()
+    log("timed %d steps: %.4f ms/step" % (args.steps, ms_step))
+
     kernel, entry, single, stage_names = run.kernel, run.entry, run.single, run.stage_names
     run.release()
 

@@ -85,6 +85,8 @@ def load():
         "msa_debug_dequant_fp8": (st, [vp, i64, vp, vp]),
         "msa_debug_read_bandwidth": (st, [vp, i64, vp, vp]),
         "msa_debug_layer_spin_limit": (st, [ctypes.c_int32]),
+        "msa_debug_layer_splits": (st, [ctypes.c_int32]),
+        "msa_decode_layer_gave_up": (st, [P, vp, sz, vp, ctypes.POINTER(ctypes.c_int64)]),
         "msa_status_string": (ctypes.c_char_p, [st]),
         "msa_last_error": (ctypes.c_char_p, []),
         "msa_version": (ctypes.c_char_p, []),
@@ -101,6 +103,7 @@ EXPORTED = ("msa_workspace_size", "msa_indexer_scores", "msa_pool_select_blocks"
             "msa_decode_layer", "msa_decode_layer_traced", "msa_decode_layer_single",
             "msa_decode_layer_single_traced", "msa_kv_insert", "msa_debug_dequant_nvfp4",
             "msa_debug_dequant_fp8", "msa_debug_read_bandwidth", "msa_debug_layer_spin_limit",
+            "msa_debug_layer_splits", "msa_decode_layer_gave_up",
             "msa_status_string", "msa_last_error", "msa_version")
 
 
@@ -252,6 +255,22 @@ def msa_debug_layer_spin_limit(polls):
     """Poll limit of msa_decode_layer_single's waits for later calls (0 =
     default)."""
     _check(load().msa_debug_layer_spin_limit(int(polls)), "msa_debug_layer_spin_limit")
+
+
+def msa_debug_layer_splits(splits):
+    """Workgroups per attention item of later msa_decode_layer_single calls
+    (1, 2 or 4; 0 = automatic)."""
+    _check(load().msa_debug_layer_splits(int(splits)), "msa_debug_layer_splits")
+
+
+def msa_decode_layer_gave_up(params, workspace, stream=None):
+    """Workgroups of the latest msa_decode_layer_single call on `workspace`
+    that gave up a bounded wait (synchronises the stream)."""
+    n = ctypes.c_int64(-1)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(load().msa_decode_layer_gave_up(ctypes.byref(params), _ptr(workspace), ws_bytes, _stream(stream),
+                                           ctypes.byref(n)), "msa_decode_layer_gave_up")
+    return int(n.value)
 
 
 def msa_debug_dequant_fp8(codes, out, stream=None):

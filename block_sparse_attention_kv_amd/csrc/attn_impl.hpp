@@ -1,6 +1,9 @@
 // attn_impl.hpp -- device code of the MSA sparse attention (gfx950); the
-// design is described at the top of attn.hip. Used by the attention kernel
-// and by the single-launch decode layer.
+// design is described at the top of attn.hip. The pieces (query operand,
+// block streaming with the online softmax, the merge of wave states, the
+// output) are used by the attention kernel (attn_body) and by the
+// single-launch decode layer (layer.hip), which splits an item's blocks
+// over several workgroups.
 #pragma once
 #include "fmt.hpp"
 #include "msa_internal.hpp"
@@ -102,109 +105,24 @@ __device__ __forceinline__ void load_v(const KvRsrc& r, const LaneOff& o, VRegs&
   V.vs = buf_load16<kAuxNT>(r.vs, o.vs, 0);
 }
 
-// ---------------------------------------------------------------- kernel
+// ---------------------------------------------------------------- pieces
 
-// The attention of workgroup wg (item wg / splits, share wg % splits) with
-// W waves; lds: the dynamic LDS region (attn_lds_bytes); tid: threadIdx.x
-// (a caller that loops over items passes it through an empty asm statement,
-// so that the lane-dependent set-up is redone per item instead of being
-// hoisted and held in registers across the loop). COHERENT: the pooled
-// scores are tagged 64-bit words written by the same grid (indexer_body),
-// read with device-scope atomic loads until they carry a.epoch, a.spin_limit
-// polls at most; an item that gives up writes NaN to its out rows and lse
-// entries and -1 to its selection instead of attending. Every thread of the
-// workgroup calls it.
-template <bool NVFP4, int W, bool COHERENT = false>
-__device__ __forceinline__ void attn_body(const AttnArgs& a, int wg, uint8_t* lds, int tid) {
-  typedef MfmaT<NVFP4> MT;
-  typedef typename MT::vec vec;
-  constexpr int NT = 64 * W;
-  __shared__ TopkLds tk;
-  __shared__ int32_t sel_lds[kTopkMax], blist[kTopkMax], plist[kTopkMax];
-  __shared__ int32_t nlist, last_lds;
-
-  const int lane = tid & (kWave - 1);
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps block loops scalar
-  const int item = wg / a.splits;   // (sequence, token, KV head)
-  const int split = wg % a.splits;  // this workgroup's share of the item's blocks
-  const int g = item % a.Hkv;
-  const int bt = item / a.Hkv;
-  const int t = bt % a.Tq, b = bt / a.Tq;
-  const int Lc = clamp_ctx(a.ctx_lens[b], a.maxb);
-  const int p = Lc - a.Tq + t;  // last visible key
-  const int h = lane & 15;      // head within the group (MFMA column)
-  const int q4 = lane >> 4;     // lane group 0..3
-
-  // ---- Q^T operand: head h, dims 32*q4 + 8s + e (issued before the
-  // selection; it does not depend on it)
-  u32x4 qraw[4];
-  {
-    const bool ok = h < a.grp;
-    const uint16_t* qrow = a.q + ((size_t)bt * a.Hq + g * a.grp + h) * kHeadDim + 32 * q4;
+// Raw Q^T operand of this lane: head g*grp + lane%16 of row bt, dims
+// 32*(lane/16) + 8s + e; zero for lanes past the group's heads.
+__device__ __forceinline__ void load_q(const AttnArgs& a, int bt, int g, int lane, u32x4 (&qraw)[4]) {
+  const int h = lane & 15, q4 = lane >> 4;
+  const bool ok = h < a.grp;
+  const uint16_t* qrow = a.q + ((size_t)bt * a.Hq + g * a.grp + h) * kHeadDim + 32 * q4;
 #pragma unroll
-    for (int s = 0; s < 4; s++) qraw[s] = ok ? reinterpret_cast<const u32x4*>(qrow)[s] : u32x4{0, 0, 0, 0};
-  }
+  for (int s = 0; s < 4; s++) qraw[s] = ok ? reinterpret_cast<const u32x4*>(qrow)[s] : u32x4{0, 0, 0, 0};
+}
 
-  // ---- selected blocks (fused: from the pooled scores; the block-table
-  // entries of all visible blocks are fetched in the same pass into an LDS
-  // page table, so the winners' pages need no second dependent load)
-  int nsel;
-  int32_t* pages = reinterpret_cast<int32_t*>(lds);  // [nvis], fused path only
-  const int32_t* bt_row = a.block_table + (size_t)b * a.maxb;
-  if (a.pooled) {
-    const int nvis = p < 0 ? 0 : p / kBlock + 1;
-    const float* src = a.pooled + (size_t)bt * a.maxb;
-    if constexpr (COHERENT) {
-      const TaggedScores tw{reinterpret_cast<const uint64_t*>(a.pooled) + (size_t)bt * a.maxb, a.epoch,
-                            a.spin_limit};
-      nsel = block_topk<NT, true>([&](int i) { return 0.0f; }, [&](int i) { return bt_row[i]; }, pages, nvis,
-                                  a.top_k, a.keep_last != 0, sel_lds, tk, tw);
-      bool gave_up = false;
-#pragma unroll
-      for (int w = 0; w < W; w++) gave_up |= tk.stale[w] != 0;
-      if (gave_up) {  // the item's results are marked invalid
-        uint16_t* orow = a.out + ((size_t)bt * a.Hq + (size_t)g * a.grp) * kHeadDim;
-        for (int i = tid; i < a.grp * kHeadDim; i += NT) orow[i] = 0x7FC0;
-        if (a.lse && tid < a.grp) a.lse[(size_t)bt * a.Hq + g * a.grp + tid] = __builtin_nanf("");
-        if (g == 0 && a.sel && tid < a.top_k) a.sel[(size_t)bt * a.top_k + tid] = -1;
-        return;
-      }
-    } else {
-      nsel = block_topk<NT>([&](int i) { return src[i]; }, [&](int i) { return bt_row[i]; }, pages, nvis,
-                            a.top_k, a.keep_last != 0, sel_lds, tk);
-    }
-    if (g == 0 && a.sel)
-      for (int k = tid; k < a.top_k; k += NT) a.sel[(size_t)bt * a.top_k + k] = k < nsel ? sel_lds[k] : -1;
-  } else {
-    if (tid < a.top_k) sel_lds[tid] = a.sel[(size_t)bt * a.top_k + tid];
-    nsel = a.top_k;
-    __syncthreads();
-  }
-  // blocks that exist, compacted, order kept; a split item keeps its share
-  // (split s of S: positions [s*per, (s+1)*per), per = ceil(count / S))
-  if (wave == 0) {
-    bool ok = false;
-    int blk = -1, page = -1;
-    if (lane < nsel && p >= 0) {
-      blk = sel_lds[lane];
-      if (blk >= 0 && blk < a.maxb && blk * kBlock <= p) {
-        page = a.pooled ? pages[blk] : bt_row[blk];
-        ok = page >= 0 && page < a.num_pages;
-      }
-    }
-    const uint64_t bal = __ballot(ok);
-    const int cnt = __popcll(bal);
-    const int per = (cnt + a.splits - 1) / a.splits, first = split * per;
-    const int pos = __popcll(bal & ((1ull << lane) - 1ull)) - first;
-    if (ok && pos >= 0 && pos < per) {
-      blist[pos] = blk;
-      plist[pos] = page;
-    }
-    if (lane == 0) nlist = max(0, min(per, cnt - first));
-  }
-
-  vec qb[4];
-  float cscale;
+// Q^T operand in the matrix-core format and the score scale (log2 domain,
+// >= 0) that the softmax applies to the raw dot products.
+template <bool NVFP4>
+__device__ __forceinline__ void convert_q(const AttnArgs& a, const u32x4 (&qraw)[4], typename MfmaT<NVFP4>::vec (&qb)[4],
+                                          float& cscale) {
+  typedef typename MfmaT<NVFP4>::vec vec;
   if constexpr (NVFP4) {
     float amax = 0.0f;
 #pragma unroll
@@ -242,18 +160,27 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, int wg, uint8_t* ld
 #pragma unroll
     for (int s = 0; s < 4; s++) qb[s] = __builtin_bit_cast(vec, qraw[s] ^ flip);
   }
-  __syncthreads();
-  const int n = __builtin_amdgcn_readfirstlane(nlist);
-  if constexpr (COHERENT) {  // single launch: the selection ran at priority 3 (see layer.hip)
-    if (2 * item >= a.B * a.Tq * a.Hkv) __builtin_amdgcn_s_setprio(1);
-    else __builtin_amdgcn_s_setprio(0);
-  }
+}
 
-  SoftmaxState st;
+__device__ __forceinline__ void init_state(SoftmaxState& st) {
   st.m = -INFINITY;
   st.l = 0.0f;
 #pragma unroll
   for (int d = 0; d < 8; d++) st.o[d] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+}
+
+// This wave's online softmax and P.V over blocks wave, wave + W, ... < n of
+// the lists blist (logical block) / plist (page) in LDS; at most MAXB blocks
+// per wave. p: the query's last visible key. Ends with st.l summed over the
+// four lanes of each head. lds: at least W * 2 KB (V-scale stages).
+template <bool NVFP4, int W, int MAXB>
+__device__ __forceinline__ void stream_blocks(const AttnArgs& a, int g, int p, const int32_t* blist,
+                                              const int32_t* plist, int n,
+                                              const typename MfmaT<NVFP4>::vec (&qb)[4], float cscale,
+                                              uint8_t* lds, int wave, int lane, SoftmaxState& st) {
+  typedef MfmaT<NVFP4> MT;
+  typedef typename MT::vec vec;
+  const int q4 = lane >> 4;
 
   // raw scores of one block (S^T tiles) -> online softmax update and the P^T
   // operand. cscale >= 0, so the max of the scaled scores is cscale times the
@@ -337,13 +264,13 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, int wg, uint8_t* ld
       load_k(r0, off, K);
       load_v(r0, off, V);
     }
-    // Fully unrolled over the wave's at most kTopkMax / W blocks: straight-line
-    // code keeps the compiler's load counters exact across blocks (a loop
-    // header merges the first and later iterations' load orders and makes
-    // every block wait for all outstanding loads). Iterations past the wave's
-    // last block run on empty resources and skip the softmax and P.V.
+    // Fully unrolled over the wave's at most MAXB blocks: straight-line code
+    // keeps the compiler's load counters exact across blocks (a loop header
+    // merges the first and later iterations' load orders and makes every
+    // block wait for all outstanding loads). Iterations past the wave's last
+    // block run on empty resources and skip the softmax and P.V.
 #pragma unroll
-    for (int it = 0; it < kTopkMax / W; it++) {
+    for (int it = 0; it < MAXB; it++) {
       const int i = wave + it * W;
       const bool valid = i < n;
       const int blk = valid ? __builtin_amdgcn_readfirstlane(blist[i]) : 0;
@@ -365,7 +292,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, int wg, uint8_t* ld
         }
         sacc[tau] = acc;
       }
-      if (it + 1 < kTopkMax / W) load_k(rn, off, K);
+      if (it + 1 < MAXB) load_k(rn, off, K);
 
       if (valid) {
         // ---- V scales to fp16 in LDS (wave-private)
@@ -403,7 +330,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, int wg, uint8_t* ld
         }
         wave_lds_sync();  // the stage is overwritten by the next block
       }
-      if (it + 1 < kTopkMax / W) load_v(rn, off, V);
+      if (it + 1 < MAXB) load_v(rn, off, V);
     }
   } else {
     for (int i = wave; i < n; i += W) {
@@ -435,8 +362,24 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, int wg, uint8_t* ld
   // ---- full row sum of this wave (the 4 lanes of a head)
   st.l += shfl_xor(st.l, 16);
   st.l += shfl_xor(st.l, 32);
+}
 
-  // ---- merge the W wave states: fixed tree, LDS slots
+// acc := log-sum-exp merge of acc and the state (m2, l2, o2), in that order.
+__device__ __forceinline__ void merge_state(SoftmaxState& acc, float m2, float l2, const f32x4 (&o2)[8]) {
+  const float M = fmaxf(acc.m, m2);
+  const float a1 = lse_weight(acc.m, M), a2 = lse_weight(m2, M);
+#pragma unroll
+  for (int d = 0; d < 8; d++) acc.o[d] = acc.o[d] * a1 + o2[d] * a2;
+  acc.l = acc.l * a1 + l2 * a2;
+  acc.m = M;
+}
+
+// Fixed-order tree merge of the W wave states through LDS slots (at least
+// W/2 * kSlotFloats floats at lds); wave 0 ends with the workgroup's state.
+// Every thread of the workgroup calls it.
+template <int W>
+__device__ __forceinline__ void merge_waves(SoftmaxState& st, uint8_t* lds, int wave, int lane) {
+  const int h = lane & 15, q4 = lane >> 4;
   float* slots = reinterpret_cast<float*>(lds);
 #pragma unroll
   for (int step = W / 2; step >= 1; step >>= 1) {
@@ -453,18 +396,125 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, int wg, uint8_t* ld
     __syncthreads();
     if (wave < step) {
       const float* sl = slots + wave * kSlotFloats;
-      const float m2 = sl[16 * kHeadDim + h], l2 = sl[16 * kHeadDim + 16 + h];
-      const float M = fmaxf(st.m, m2);
-      const float a1 = lse_weight(st.m, M), a2 = lse_weight(m2, M);
+      f32x4 o2[8];
 #pragma unroll
-      for (int d = 0; d < 8; d++) {
-        const f32x4 o2 = *reinterpret_cast<const f32x4*>(sl + h * kHeadDim + 16 * d + 4 * q4);
-        st.o[d] = st.o[d] * a1 + o2 * a2;
-      }
-      st.l = st.l * a1 + l2 * a2;
-      st.m = M;
+      for (int d = 0; d < 8; d++) o2[d] = *reinterpret_cast<const f32x4*>(sl + h * kHeadDim + 16 * d + 4 * q4);
+      merge_state(st, sl[16 * kHeadDim + h], sl[16 * kHeadDim + 16 + h], o2);
     }
   }
+}
+
+// bf16 output rows (and lse) of KV head g of row bt from wave 0's state
+// (called by wave 0 only).
+__device__ __forceinline__ void write_out(const AttnArgs& a, int bt, int g, const SoftmaxState& st, int lane) {
+  const int h = lane & 15, q4 = lane >> 4;
+  if (h >= a.grp) return;
+  const size_t row = (size_t)bt * a.Hq + g * a.grp + h;
+  const bool empty = !(st.l > 0.0f);
+  const float inv = empty ? 0.0f : a.v_scale_mul / st.l;
+  uint16_t* orow = a.out + row * kHeadDim;
+#pragma unroll
+  for (int d = 0; d < 8; d++) {
+    const f32x4 o = st.o[d];
+    uint2 pk;
+    pk.x = f32x2_to_bf16x2(o[0] * inv, o[1] * inv);
+    pk.y = f32x2_to_bf16x2(o[2] * inv, o[3] * inv);
+    *reinterpret_cast<uint2*>(orow + 16 * d + 4 * q4) = pk;
+  }
+  if (a.lse && q4 == 0) a.lse[row] = empty ? -INFINITY : (st.m + __log2f(st.l)) * 0.69314718055994530942f;
+}
+
+// NaN output rows and lse of KV head g of row bt: the item's inputs never
+// arrived (a bounded wait gave up). Threads tid < NT share the writes.
+__device__ __forceinline__ void write_invalid(const AttnArgs& a, int bt, int g, int tid, int NT) {
+  uint16_t* orow = a.out + ((size_t)bt * a.Hq + (size_t)g * a.grp) * kHeadDim;
+  for (int i = tid; i < a.grp * kHeadDim; i += NT) orow[i] = 0x7FC0;
+  if (a.lse && tid < a.grp) a.lse[(size_t)bt * a.Hq + g * a.grp + tid] = __builtin_nanf("");
+}
+
+// ---------------------------------------------------------------- kernel
+
+// The attention of workgroup wg (item wg / splits, share wg % splits) with
+// W waves; lds: the dynamic LDS region (attn_lds_bytes); tid: threadIdx.x.
+// With a.pooled the workgroup first selects its query token's blocks from
+// the pooled scores; otherwise it reads them from a.sel. Every thread of the
+// workgroup calls it.
+template <bool NVFP4, int W>
+__device__ __forceinline__ void attn_body(const AttnArgs& a, int wg, uint8_t* lds, int tid) {
+  typedef MfmaT<NVFP4> MT;
+  typedef typename MT::vec vec;
+  constexpr int NT = 64 * W;
+  __shared__ TopkLds tk;
+  __shared__ int32_t sel_lds[kTopkMax], blist[kTopkMax], plist[kTopkMax];
+  __shared__ int32_t nlist, last_lds;
+
+  const int lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps block loops scalar
+  const int item = wg / a.splits;   // (sequence, token, KV head)
+  const int split = wg % a.splits;  // this workgroup's share of the item's blocks
+  const int g = item % a.Hkv;
+  const int bt = item / a.Hkv;
+  const int b = bt / a.Tq;
+  const int Lc = clamp_ctx(a.ctx_lens[b], a.maxb);
+  const int p = Lc - a.Tq + bt % a.Tq;  // last visible key
+  const int h = lane & 15;      // head within the group (MFMA column)
+  const int q4 = lane >> 4;     // lane group 0..3
+
+  // ---- Q^T operand (issued before the selection; it does not depend on it)
+  u32x4 qraw[4];
+  load_q(a, bt, g, lane, qraw);
+
+  // ---- selected blocks (fused: from the pooled scores; the block-table
+  // entries of all visible blocks are fetched in the same pass into an LDS
+  // page table, so the winners' pages need no second dependent load)
+  int nsel;
+  int32_t* pages = reinterpret_cast<int32_t*>(lds);  // [nvis], fused path only
+  const int32_t* bt_row = a.block_table + (size_t)b * a.maxb;
+  if (a.pooled) {
+    const int nvis = p < 0 ? 0 : p / kBlock + 1;
+    const float* src = a.pooled + (size_t)bt * a.maxb;
+    nsel = block_topk<NT>([&](int i) { return src[i]; }, [&](int i) { return bt_row[i]; }, pages, nvis,
+                          a.top_k, a.keep_last != 0, sel_lds, tk);
+    if (g == 0 && a.sel)
+      for (int k = tid; k < a.top_k; k += NT) a.sel[(size_t)bt * a.top_k + k] = k < nsel ? sel_lds[k] : -1;
+  } else {
+    if (tid < a.top_k) sel_lds[tid] = a.sel[(size_t)bt * a.top_k + tid];
+    nsel = a.top_k;
+    __syncthreads();
+  }
+  // blocks that exist, compacted, order kept; a split item keeps its share
+  // (split s of S: positions [s*per, (s+1)*per), per = ceil(count / S))
+  if (wave == 0) {
+    bool ok = false;
+    int blk = -1, page = -1;
+    if (lane < nsel && p >= 0) {
+      blk = sel_lds[lane];
+      if (blk >= 0 && blk < a.maxb && blk * kBlock <= p) {
+        page = a.pooled ? pages[blk] : bt_row[blk];
+        ok = page >= 0 && page < a.num_pages;
+      }
+    }
+    const uint64_t bal = __ballot(ok);
+    const int cnt = __popcll(bal);
+    const int per = (cnt + a.splits - 1) / a.splits, first = split * per;
+    const int pos = __popcll(bal & ((1ull << lane) - 1ull)) - first;
+    if (ok && pos >= 0 && pos < per) {
+      blist[pos] = blk;
+      plist[pos] = page;
+    }
+    if (lane == 0) nlist = max(0, min(per, cnt - first));
+  }
+
+  vec qb[4];
+  float cscale;
+  convert_q<NVFP4>(a, qraw, qb, cscale);
+  __syncthreads();
+  const int n = __builtin_amdgcn_readfirstlane(nlist);
+
+  SoftmaxState st;
+  init_state(st);
+  stream_blocks<NVFP4, W, kTopkMax / W>(a, g, p, blist, plist, n, qb, cscale, lds, wave, lane, st);
+  merge_waves<W>(st, lds, wave, lane);
 
   if (a.splits > 1) {
     // ---- split item: publish this workgroup's state; the last of the
@@ -523,21 +573,7 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, int wg, uint8_t* ld
   }
 
   // ---- write bf16 output (and lse) for the real heads
-  if (wave == 0 && h < a.grp) {
-    const size_t row = (size_t)bt * a.Hq + g * a.grp + h;
-    const bool empty = !(st.l > 0.0f);
-    const float inv = empty ? 0.0f : a.v_scale_mul / st.l;
-    uint16_t* orow = a.out + row * kHeadDim;
-#pragma unroll
-    for (int d = 0; d < 8; d++) {
-      const f32x4 o = st.o[d];
-      uint2 pk;
-      pk.x = f32x2_to_bf16x2(o[0] * inv, o[1] * inv);
-      pk.y = f32x2_to_bf16x2(o[2] * inv, o[3] * inv);
-      *reinterpret_cast<uint2*>(orow + 16 * d + 4 * q4) = pk;
-    }
-    if (a.lse && q4 == 0) a.lse[row] = empty ? -INFINITY : (st.m + __log2f(st.l)) * 0.69314718055994530942f;
-  }
+  if (wave == 0) write_out(a, bt, g, st, lane);
 }
 
 // Dynamic LDS: the pooled scores of one token (fused selection), the

@@ -1,41 +1,64 @@
 // layer.hip -- the decode step of one layer in a single launch (gfx950):
-// indexer + block max-pool, then selection and sparse attention per
-// (sequence, query token, KV head), ordered by tags on the pooled scores
-// instead of a kernel boundary.
+// indexer + block max-pool, top-k selection, then sparse attention per
+// (sequence, query token, KV head), ordered by tags on the data the
+// workgroups exchange instead of kernel boundaries.
 //
 // [upstreambeat page "vLLM turns MiniMax's day-zero promise into
 // GPU-specific serving code", section "What changed": on MI355X the decode
 // path runs as one launch (the "mono" kernel) to save launch overhead.]
 //
-// Grid. Workgroups 0 .. n_idx-1 run the persistent indexer scan
-// (indexer_impl.hpp) over the batch's (sequence, block) work exactly as the
-// indexer kernel does, with two workgroups per compute unit (the register
-// budget of the attention) and two blocks of keys in flight per wave. Every
-// pooled score is published as one 64-bit word, the call's epoch in the high
-// half and the fp32 score in the low half. Workgroups n_idx + i take
-// attention item i (attn_impl.hpp, 4 waves): they read the pooled scores of
-// their query token right away and read again any word that does not carry
-// the epoch yet, then run the selection and the attention. No flag, counter
-// or fence is involved, a word left by an older call holds another epoch (the
-// workspace is never cleared), and an item needs no knowledge of which
-// indexer workgroups cover its sequence. The attention workgroups come after
-// every indexer workgroup in dispatch order and the indexer workgroups wait
-// on nothing, so the waits end; as indexer workgroups retire, attention
-// workgroups take their slots. A wait is also bounded (about a second; a
-// debug export can lower the bound): an item that gives up writes NaN
-// outputs and lse and a selection of -1.
+// The grid starts with n_idx indexer workgroups: the persistent scan of
+// indexer_impl.hpp over the batch's (sequence, block) work, two workgroups
+// per compute unit, two blocks of keys in flight per wave. Every pooled score
+// is published as one 64-bit word: the call's epoch in the high half, the
+// fp32 score in the low half. The rest of the grid has one of two shapes.
+//
+// Fused (batches with at least one (sequence, token, KV head) item per
+// compute unit): one workgroup per item reads its token's tagged pooled
+// scores (reading again any word that does not carry the epoch yet), selects
+// the top-k blocks itself (topk.hpp) and attends, four blocks per wave. The
+// KV heads of a token repeat the cheap selection rather than wait for one
+// another.
+//
+// Split (fewer items, where one item per workgroup would leave most of the
+// chip idle and a lone wave streams a block in several microseconds): per
+// query token, NSUB selector workgroups followed by H_kv * S attention
+// workgroups.
+//   selector j     takes blocks [1024 j, 1024 (j+1)) of the token's visible
+//                  blocks and publishes its top-k of them as a tagged
+//                  candidate record: a header word (count, give-up flag) and,
+//                  per candidate, its ranking key (the order-preserving image
+//                  of its pooled score), its logical block and its page.
+//   attention      (KV head g, split s < S) reads the token's NSUB records
+//                  (one round trip once they are there), takes the top-k of
+//                  all candidates -- the top-k of the whole context, since
+//                  every winner is among its range's top-k -- and attends to
+//                  positions [s*per, (s+1)*per) of the selected blocks (per =
+//                  ceil(count / S)), one block per wave. Splits s < S-1
+//                  publish their merged softmax state (m, l, O of every head
+//                  of the group) as tagged words; the last split's waves read
+//                  them in parallel and wave 0 merges splits 0, 1, ..., S-1
+//                  in that order, so the result does not depend on timing.
+// Every wait is on a workgroup earlier in dispatch order, and the indexer
+// workgroups wait on nothing: with each XCD dispatching its workgroups in
+// order, the earliest unfinished workgroup of the grid can always run to its
+// end, so every wait ends. A wait is also bounded (about a second; a debug
+// export can lower the bound): a workgroup that gives up marks its results
+// invalid (NaN outputs and lse, selection -1) and counts itself in the
+// workspace's give-up word, which msa_decode_layer_gave_up reads.
 //
 // Coherence. The compute units of different XCDs have separate L2 caches, so
 // a device-scope release / acquire fence writes back / invalidates the L2;
 // one per workgroup costs several microseconds at the end of the scan. Here
 // only device-scope relaxed atomics cross workgroups: 64-bit atomic stores
-// of the tagged scores (written through to the coherence point) and 64-bit
-// atomic loads; a word is valid by itself, so no ordering between words is
-// needed. No plain load or store touches the pooled scores in this kernel.
+// of tagged words (written through to the coherence point) and 64-bit atomic
+// loads. Every word is valid by itself (its tag says which call wrote it),
+// so no ordering between words is needed, and no plain load or store
+// touches them.
 //
-// The pooled scores and the selection equal the two-kernel path's bit for
-// bit, and so does the output wherever that path's attention also runs 4
-// waves per item (batches with at least two items per compute unit).
+// The selection equals the two-kernel path's bit for bit; in the fused shape
+// so does the output wherever that path's attention also runs 4 waves per
+// item (batches with at least two items per compute unit).
 // Supported: NVFP4 K/V, FP8 or NVFP4 indexer keys, q_len <= 4.
 #include <atomic>
 
@@ -47,81 +70,527 @@ namespace msa {
 namespace {
 
 constexpr int kLayerWaves = 4;
+constexpr int kLayerThreads = 64 * kLayerWaves;
 constexpr int kLayerWgsPerCu = 2;
-constexpr int kSpinLimit = 1 << 20;  // polls of one chunk of pooled scores (a memory round trip each)
+constexpr int kSpinLimit = 1 << 20;  // polls of one chunk of tagged words (a memory round trip each)
+constexpr int kSubBlocks = 1024;     // blocks per selector: one 256-block chunk per wave
+constexpr int kCandWords = 1 + 3 * kTopkMax;  // words of a candidate record in use
 
 // Poll limit of the next launches (0: kSpinLimit); set by a debug export.
 std::atomic<int> g_spin_limit{0};
 
 struct LayerArgs {
   IndexerArgs ia;
-  AttnArgs aa;  // aa.epoch: the tag of the pooled scores; aa.spin_limit: polls of one score
-  int idx_wgs;  // workgroups running the indexer
+  AttnArgs aa;            // aa.pooled: the tagged pooled words; aa.epoch: the call's tag;
+                          // aa.spin_limit: polls before a wait gives up; aa.splits: S
+  LayerScratch ws;
+  int idx_wgs;            // workgroups running the indexer
+  int nsub;               // split shape: selectors per query token (0: fused shape)
 };
 
-template <int KF, int HP, int TQ>
-__global__ __launch_bounds__(64 * kLayerWaves, kLayerWgsPerCu) void decode_layer_single_kernel(LayerArgs L) {
+__device__ __forceinline__ uint64_t load_word(const uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_word(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Counts one workgroup that gave up a wait in the give-up word
+// (epoch << 32 | count): a word of another call restarts the count. Every
+// failed exchange is another workgroup's success, so the loop ends; its
+// bound only guards against the unexpected.
+__device__ void report_give_up(const LayerArgs& L) {
+  unsigned long long* w = L.ws.gave_up;
+  const unsigned long long fresh = (unsigned long long)L.aa.epoch << 32;
+  unsigned long long seen = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (int i = 0; i < (1 << 16); i++) {
+    const unsigned long long want = ((seen >> 32) == L.aa.epoch ? seen : fresh) + 1ull;
+    const unsigned long long prev = atomicCAS(w, seen, want);
+    if (prev == seen) break;
+    seen = prev;
+  }
+}
+
+// Last visible key of query token `tok` (sequence tok / Tq).
+__device__ __forceinline__ int query_pos(const AttnArgs& a, int tok) {
+  return clamp_ctx(a.ctx_lens[tok / a.Tq], a.maxb) - a.Tq + tok % a.Tq;
+}
+
+// Q^T operand, the attention of the W waves over the LDS block lists and
+// the merge of the wave states; wave 0 ends with the workgroup's state.
+template <int MAXB>
+__device__ __forceinline__ void attend_list(const AttnArgs& a, int tok, int g, int p, const u32x4 (&qraw)[4],
+                                            const int32_t* blist, const int32_t* plist, int n, uint8_t* lds,
+                                            int wave, int lane, SoftmaxState& st) {
+  MfmaT<true>::vec qb[4];
+  float cscale;
+  convert_q<true>(a, qraw, qb, cscale);
+  init_state(st);
+  stream_blocks<true, kLayerWaves, MAXB>(a, g, p, blist, plist, n, qb, cscale, lds, wave, lane, st);
+  merge_waves<kLayerWaves>(st, lds, wave, lane);
+}
+
+// Leaves the top wave priority once the blocks are known: the later half of
+// the items, dispatched last, ends the kernel, and its waves share compute
+// units with older attention waves that win issue arbitration by age.
+__device__ __forceinline__ void drop_priority(const AttnArgs& a, int item) {
+  if (2 * item >= a.B * a.Tq * a.Hkv) __builtin_amdgcn_s_setprio(1);
+  else __builtin_amdgcn_s_setprio(0);
+}
+
+// ---------------------------------------------------------------- fused shape
+
+// Item `item` = (token, KV head): selection from the token's tagged pooled
+// scores, then attention over all selected blocks.
+__device__ void fused_item(const LayerArgs& L, int item, uint8_t* lds) {
+  const AttnArgs& a = L.aa;
+  __shared__ TopkLds tk;
+  __shared__ int32_t sel_lds[kTopkMax], blist[kTopkMax], plist[kTopkMax];
+  __shared__ int32_t nlist;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = item % a.Hkv, tok = item / a.Hkv;
+  const int b = tok / a.Tq;
+  const int p = query_pos(a, tok);
+  u32x4 qraw[4];
+  load_q(a, tok, g, lane, qraw);  // issued first: it does not depend on the selection
+
+  const int nvis = p < 0 ? 0 : p / kBlock + 1;
+  int32_t* pages = reinterpret_cast<int32_t*>(lds);  // [nvis]: block-table entries, fetched with the scores
+  const int32_t* bt_row = a.block_table + (size_t)b * a.maxb;
+  const TaggedScores tw{reinterpret_cast<const uint64_t*>(a.pooled) + (size_t)tok * a.maxb, a.epoch,
+                        a.spin_limit};
+  const int nsel = block_topk<kLayerThreads, true>([&](int i) { return 0.0f; }, [&](int i) { return bt_row[i]; },
+                                                   pages, nvis, a.top_k, a.keep_last != 0, sel_lds, tk, tw);
+  bool stale = false;
+#pragma unroll
+  for (int w = 0; w < kLayerWaves; w++) stale |= tk.stale[w] != 0;
+  if (stale) {  // the item's results are marked invalid
+    write_invalid(a, tok, g, tid, kLayerThreads);
+    if (g == 0 && a.sel && tid < a.top_k) a.sel[(size_t)tok * a.top_k + tid] = -1;
+    if (tid == 0) report_give_up(L);
+    return;
+  }
+  if (g == 0 && a.sel && tid < a.top_k) a.sel[(size_t)tok * a.top_k + tid] = tid < nsel ? sel_lds[tid] : -1;
+  // attended blocks: selected, visible, with a page in range; ascending
+  if (wave == 0) {
+    bool ok = false;
+    int blk = -1, page = -1;
+    if (lane < nsel) {
+      blk = sel_lds[lane];
+      page = pages[blk];
+      ok = page >= 0 && page < a.num_pages;
+    }
+    const uint64_t bal = __ballot(ok);
+    const int pos = __popcll(bal & ((1ull << lane) - 1ull));
+    if (ok) {
+      blist[pos] = blk;
+      plist[pos] = page;
+    }
+    if (lane == 0) nlist = __popcll(bal);
+  }
+  __syncthreads();
+  drop_priority(a, item);
+  SoftmaxState st;
+  attend_list<kTopkMax / kLayerWaves>(a, tok, g, p, qraw, blist, plist, __builtin_amdgcn_readfirstlane(nlist), lds,
+                                      wave, lane, st);
+  if (wave == 0) write_out(a, tok, g, st, lane);
+}
+
+// ---------------------------------------------------------------- split shape
+
+__device__ __forceinline__ uint64_t* cand_record(const LayerArgs& L, int tok, int j) {
+  return L.ws.records + ((size_t)tok * L.nsub + j) * kRecordWords;
+}
+
+// Selector j of query token `tok`: the top-k of the token's visible blocks
+// [1024 j, 1024 (j+1)), published as a candidate record.
+__device__ void select_range(const LayerArgs& L, int tok, int j, uint8_t* lds) {
+  const AttnArgs& a = L.aa;
+  __shared__ TopkLds tk;
+  __shared__ int32_t sel_lds[kTopkMax];
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int p = query_pos(a, tok);
+  const int nvis = p < 0 ? 0 : p / kBlock + 1;
+  const int lo = min(nvis, j * kSubBlocks), hi = min(nvis, lo + kSubBlocks);
+  const int n = hi - lo;
+  const bool forced = a.keep_last != 0 && hi == nvis;  // the range holds the query's own block
+  int32_t* pages = reinterpret_cast<int32_t*>(lds);   // [n]
+  const int32_t* bt_row = a.block_table + (size_t)(tok / a.Tq) * a.maxb + lo;
+  const uint64_t* words = reinterpret_cast<const uint64_t*>(a.pooled) + (size_t)tok * a.maxb + lo;
+  bool stale = false;
+  int cnt;
+  if (n > a.top_k) {
+    block_topk<kLayerThreads, true>([&](int i) { return 0.0f; }, [&](int i) { return bt_row[i]; }, pages, n,
+                                    a.top_k, forced, sel_lds, tk, TaggedScores{words, a.epoch, a.spin_limit});
+#pragma unroll
+    for (int w = 0; w < kLayerWaves; w++) stale |= tk.stale[w] != 0;
+    cnt = a.top_k;  // keys of the winners: tk.fin[0 .. top_k)
+  } else {
+    // every block of the range is a candidate: read its score directly
+    if (wave == 0) {
+      uint64_t w = 0;
+      bool got = true;
+      if (lane < n) w = load_word(words + lane);
+      for (int polls = 0;;) {
+        const bool miss = lane < n && (uint32_t)(w >> 32) != a.epoch;
+        if (__ballot(miss) == 0ull) break;
+        if (++polls >= a.spin_limit) {
+          got = false;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+        if (miss) w = load_word(words + lane);
+      }
+      if (lane < n) {
+        tk.fin[lane] = block_key(__uint_as_float((uint32_t)w), lane, forced && lane == n - 1);
+        pages[lane] = bt_row[lane];
+      }
+      if (lane == 0) tk.stale[0] = got ? 0 : 1;
+    }
+    __syncthreads();
+    stale = tk.stale[0] != 0;
+    cnt = n;
+  }
+  if (wave != 0) return;
+  const uint64_t tag = (uint64_t)a.epoch << 32;
+  uint64_t* rec = cand_record(L, tok, j);
+  if (!stale && lane < cnt) {
+    const uint64_t key = tk.fin[lane];
+    const int local = (int)(0xFFFFFFFFu - (uint32_t)key);
+    const int page = pages[local];
+    const bool ok = page >= 0 && page < a.num_pages;
+    store_word(rec + 1 + 3 * lane, tag | (uint32_t)(key >> 32));
+    store_word(rec + 2 + 3 * lane, tag | (uint32_t)(lo + local));
+    store_word(rec + 3 + 3 * lane, tag | (ok ? (uint32_t)page : 0xFFFFFFFFu));
+  } else if (lane < kTopkMax) {  // unused entries carry the tag too: a reader polls all of them
+    store_word(rec + 1 + 3 * lane, tag);
+    store_word(rec + 2 + 3 * lane, tag | 0xFFFFFFFFu);
+    store_word(rec + 3 + 3 * lane, tag | 0xFFFFFFFFu);
+  }
+  if (lane == 0) store_word(rec, tag | (stale ? kRecordStale : 0u) | (uint32_t)(stale ? 0 : cnt));
+  if (stale && lane == 0) report_give_up(L);
+}
+
+// Tagged partial softmax state of one split: per head h, 128 O words, m, l
+// (a row of kPartRow words); lane (h, q4) holds O dims 16d + 4*q4 + r.
+__device__ __forceinline__ uint64_t* partial_row(const LayerArgs& L, int item, int split, int h) {
+  return L.ws.partials + (((size_t)item * (L.aa.splits - 1) + split) * 16 + h) * kPartRow;
+}
+
+// Attention of KV head g of query token tok, split `split` of S.
+template <int MAXB>
+__device__ void split_item(const LayerArgs& L, int tok, int g, int split, uint8_t* lds) {
+  const AttnArgs& a = L.aa;
+  __shared__ uint64_t cand[kTopkMax * 8];   // winners of the final merge (keys), then their order
+  __shared__ int32_t cblk[kTopkMax * 8], cpage[kTopkMax * 8];
+  __shared__ int32_t blist[kTopkMax], plist[kTopkMax], sel_all[kTopkMax];
+  __shared__ int32_t ccount[8];             // candidates per record
+  __shared__ int32_t nlist, bad, gave[kLayerWaves];
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane & 15, q4 = lane >> 4;
+  const int S = a.splits;
+  const int item = tok * a.Hkv + g;
+  const int p = query_pos(a, tok);
+  const uint64_t tag = (uint64_t)a.epoch << 32;
+
+  u32x4 qraw[4];
+  load_q(a, tok, g, lane, qraw);  // issued first: it does not depend on the selection
+
+  // ---- the token's candidate records -> the top-k blocks -> this split's share
+  if (wave == 0) {
+    const int nrec = L.nsub;
+    const int nw = nrec * kRecordWords;  // words to read (whole padded records)
+    const uint64_t* src = cand_record(L, tok, 0);
+    // up to 8 records of 56 words: 7 words per lane
+    uint64_t w[7];
+    bool got = true, stale = false;
+    for (int polls = 0;; polls++) {
+      bool miss = false;
+#pragma unroll
+      for (int i = 0; i < 7; i++) {
+        const int x = lane + 64 * i;
+        const bool used = x < nw && x % kRecordWords < kCandWords;
+        if (polls == 0 || (used && (uint32_t)(w[i] >> 32) != a.epoch)) w[i] = used ? load_word(src + x) : tag;
+        miss |= (uint32_t)(w[i] >> 32) != a.epoch;
+      }
+      if (__ballot(miss) == 0ull) break;
+      if (polls + 1 >= a.spin_limit) {
+        got = false;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+    // candidates: record r entry e at words 1 + 3e (key), 2 + 3e (block), 3 + 3e (page)
+#pragma unroll
+    for (int i = 0; i < 7; i++) {
+      const int x = lane + 64 * i;
+      if (x < nw) {
+        const int r = x / kRecordWords, o = x % kRecordWords;
+        if (o == 0) {
+          stale |= ((uint32_t)w[i] & kRecordStale) != 0u || ((uint32_t)w[i] & 0xFFFFu) > kTopkMax;
+          ccount[r] = (int)((uint32_t)w[i] & 0xFFFFu);
+        }
+        if (o >= 1 && o < kCandWords) {
+          const int e = (o - 1) / 3, f = (o - 1) % 3, c = r * kTopkMax + e;
+          if (f == 0) cand[c] = (uint32_t)w[i];
+          else if (f == 1) cblk[c] = (int)(uint32_t)w[i];
+          else cpage[c] = (int)(uint32_t)w[i];
+        }
+      }
+    }
+    stale = __ballot(stale) != 0ull || !got;
+    wave_lds_sync();
+    // keys of the valid candidates: (ranking key << 32) | (8191 - block) << 7 | slot
+    uint64_t k[2];
+    int total = 0;
+#pragma unroll
+    for (int s2 = 0; s2 < 2; s2++) {
+      const int c = lane + 64 * s2;
+      const int r = c / kTopkMax, e = c % kTopkMax;
+      bool valid = false;
+      if (r < nrec && !stale && e < ccount[r]) {
+        const int blk = cblk[c];
+        valid = blk >= 0 && blk < a.maxb && blk * kBlock <= p;
+      }
+      k[s2] = valid ? (cand[c] << 32) | ((uint64_t)(8191 - cblk[c]) << 7) | (uint64_t)c : 0ull;
+      total += __popcll(__ballot(valid));
+    }
+    const int K = min(a.top_k, total);
+    int cnt = 0;
+    if (K > 0) {
+      const uint64_t T = kth_threshold<2>(k, K);
+      __shared__ uint64_t fin[kTopkMax];
+      compact_ge<2>(k, T, fin);
+      wave_lds_sync();
+      // ascending block order: the rank of each winner among the winners;
+      // then the attended ones (page present) keep that order
+      __shared__ int32_t sblk[kTopkMax], spage[kTopkMax];
+      int rank = 0;
+      if (lane < K) {
+        const int c = (int)(fin[lane] & 127u);
+        const int blk = cblk[c];
+        for (int q = 0; q < K; q++) rank += (8191 - (int)((fin[q] >> 7) & 8191u)) < blk;
+        sblk[rank] = blk;
+        spage[rank] = cpage[c];
+        sel_all[rank] = blk;
+      }
+      wave_lds_sync();
+      // lane r: the winner of rank r
+      const int blk = lane < K ? sblk[lane] : -1, page = lane < K ? spage[lane] : -1;
+      const bool ok = lane < K && page >= 0 && page < a.num_pages;
+      const uint64_t bal = __ballot(ok);
+      const int apos = __popcll(bal & ((1ull << lane) - 1ull));
+      cnt = __popcll(bal);
+      const int per = (cnt + S - 1) / S, first = split * per;
+      if (ok && apos >= first && apos < first + per) {
+        blist[apos - first] = blk;
+        plist[apos - first] = page;
+      }
+      if (lane == 0) nlist = max(0, min(per, cnt - first));
+    } else if (lane == 0) {
+      nlist = 0;
+    }
+    if (split == 0 && g == 0 && a.sel && lane < a.top_k) {
+      wave_lds_sync();
+      a.sel[(size_t)tok * a.top_k + lane] = (!stale && lane < K) ? sel_all[lane] : -1;
+    }
+    if (lane == 0) {
+      bad = stale ? 1 : 0;
+      if (!got) report_give_up(L);
+    }
+  }
+  __syncthreads();
+  if (bad) {
+    write_invalid(a, tok, g, tid, kLayerThreads);
+    return;
+  }
+  drop_priority(a, item);
+  SoftmaxState st;
+  attend_list<MAXB>(a, tok, g, p, qraw, blist, plist, __builtin_amdgcn_readfirstlane(nlist), lds, wave, lane, st);
+  if (S == 1) {
+    if (wave == 0) write_out(a, tok, g, st, lane);
+    return;
+  }
+  if (split < S - 1) {  // publish this split's state
+    if (wave != 0) return;
+    uint64_t* row = partial_row(L, item, split, h);
+#pragma unroll
+    for (int d = 0; d < 8; d++)
+#pragma unroll
+      for (int r = 0; r < 4; r++) store_word(row + 16 * d + 4 * q4 + r, tag | __float_as_uint(st.o[d][r]));
+    if (q4 == 0) {
+      store_word(row + 128, tag | __float_as_uint(st.m));
+      store_word(row + 129, tag | __float_as_uint(st.l));
+    }
+    return;
+  }
+  // last split: wave w (1 <= w < S) reads split w-1's state into LDS slot
+  // w-1; wave 0 then merges splits 0 .. S-2 and its own, in that order.
+  // Each reading wave first waits on one word of its split (head 0's l,
+  // stored last), so that a state still being written costs one load per
+  // poll, not a whole row.
+  float* slots = reinterpret_cast<float*>(lds);
+  __syncthreads();  // the wave-merge slots are free again
+  if (wave >= 1 && wave < S) {
+    const uint64_t* row = partial_row(L, item, wave - 1, h);
+    uint64_t wo[32], wm = 0, wl = 0;
+    bool got = false;
+    {
+      const uint64_t* last = partial_row(L, item, wave - 1, 0) + 129;
+      for (int polls = 0; polls < a.spin_limit; polls++) {
+        if ((uint32_t)(__builtin_amdgcn_readfirstlane((int)(load_word(last) >> 32))) == a.epoch) break;
+        __builtin_amdgcn_s_sleep(1);
+      }
+    }
+    for (int polls = 0; polls < a.spin_limit; polls++) {
+      if (polls) __builtin_amdgcn_s_sleep(1);
+      bool miss = false;
+#pragma unroll
+      for (int d = 0; d < 8; d++)
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+          wo[4 * d + r] = load_word(row + 16 * d + 4 * q4 + r);
+          miss |= (uint32_t)(wo[4 * d + r] >> 32) != a.epoch;
+        }
+      wm = load_word(row + 128);
+      wl = load_word(row + 129);
+      miss |= (uint32_t)(wm >> 32) != a.epoch || (uint32_t)(wl >> 32) != a.epoch;
+      if (__ballot(miss) == 0ull) {
+        got = true;
+        break;
+      }
+    }
+    float* sl = slots + (wave - 1) * kSlotFloats;
+#pragma unroll
+    for (int d = 0; d < 8; d++)
+#pragma unroll
+      for (int r = 0; r < 4; r++) sl[h * kHeadDim + 16 * d + 4 * q4 + r] = __uint_as_float((uint32_t)wo[4 * d + r]);
+    if (q4 == 0) {
+      sl[16 * kHeadDim + h] = __uint_as_float((uint32_t)wm);
+      sl[16 * kHeadDim + 16 + h] = __uint_as_float((uint32_t)wl);
+    }
+    if (lane == 0) gave[wave] = got ? 0 : 1;
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  bool lost = false;
+  for (int w = 1; w < S; w++) lost |= gave[w] != 0;
+  if (lost) {
+    write_invalid(a, tok, g, lane, kWave);
+    if (lane == 0) report_give_up(L);
+    return;
+  }
+  SoftmaxState acc;
+  init_state(acc);
+  for (int s = 0; s < S - 1; s++) {
+    const float* sl = slots + s * kSlotFloats;
+    f32x4 o2[8];
+#pragma unroll
+    for (int d = 0; d < 8; d++) o2[d] = *reinterpret_cast<const f32x4*>(sl + h * kHeadDim + 16 * d + 4 * q4);
+    merge_state(acc, sl[16 * kHeadDim + h], sl[16 * kHeadDim + 16 + h], o2);
+  }
+  merge_state(acc, st.m, st.l, st.o);
+  write_out(a, tok, g, acc, lane);
+}
+
+template <int KF, int HP, int TQ, int MAXB>
+__global__ __launch_bounds__(kLayerThreads, kLayerWgsPerCu) void decode_layer_single_kernel(LayerArgs L) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   if ((int)blockIdx.x < L.idx_wgs) {
     indexer_body<KF, HP, TQ, false, 2, true>(L.ia, reinterpret_cast<int32_t*>(lds), blockIdx.x, L.idx_wgs,
                                              L.aa.epoch);
     return;
   }
-  // Until its selection is made an item runs at the highest wave priority:
-  // reading the pooled scores and the selection are a chain of dependent
-  // steps with little issue work, on the critical path of every item, while
-  // the waves it shares a compute unit with stream keys. attn_body drops the
-  // priority once the blocks are known (to 1 for the later half of the
-  // items, which is dispatched last and ends the kernel: its waves share
-  // compute units with older attention waves of the first half, which win
-  // issue arbitration by age; to 0 for the rest).
+  const int r = (int)blockIdx.x - L.idx_wgs;
+  // Selection, and an attention item until it knows its blocks, run at the
+  // highest wave priority: reading tagged words and selecting are a chain of
+  // dependent steps with little issue work, on the critical path of every
+  // item, while the waves they share a compute unit with stream keys.
   __builtin_amdgcn_s_setprio(3);
-  attn_body<true, kLayerWaves, true>(L.aa, blockIdx.x - L.idx_wgs, lds, (int)threadIdx.x);
+  if (L.nsub == 0) {
+    if constexpr (MAXB == kTopkMax / kLayerWaves) fused_item(L, r, lds);
+    return;
+  }
+  const int per_tok = L.nsub + L.aa.Hkv * L.aa.splits;
+  const int tok = r / per_tok, k = r - tok * per_tok;
+  if (k < L.nsub) {
+    select_range(L, tok, k, lds);
+    return;
+  }
+  split_item<MAXB>(L, tok, (k - L.nsub) / L.aa.splits, (k - L.nsub) % L.aa.splits, lds);
+}
+
+template <int KF, int HP, int TQ>
+void* pick_maxb(int maxb) {
+  switch (maxb) {
+    case 4: return reinterpret_cast<void*>(decode_layer_single_kernel<KF, HP, TQ, 4>);
+    case 2: return reinterpret_cast<void*>(decode_layer_single_kernel<KF, HP, TQ, 2>);
+    case 1: return reinterpret_cast<void*>(decode_layer_single_kernel<KF, HP, TQ, 1>);
+  }
+  return nullptr;
 }
 
 template <int KF, int HP>
-hipError_t launch_single_hp(const LayerArgs& L, int items, hipStream_t s, const KTimer* tm) {
-  void (*kern)(LayerArgs) = nullptr;
-  switch (L.ia.Tq) {
-    case 1: kern = decode_layer_single_kernel<KF, HP, 1>; break;
-    case 2: kern = decode_layer_single_kernel<KF, HP, 2>; break;
-    case 3: kern = decode_layer_single_kernel<KF, HP, 3>; break;
-    case 4: kern = decode_layer_single_kernel<KF, HP, 4>; break;
-    default: return hipErrorInvalidValue;
+void* pick_tq(int tq, int maxb) {
+  switch (tq) {
+    case 1: return pick_maxb<KF, HP, 1>(maxb);
+    case 2: return pick_maxb<KF, HP, 2>(maxb);
+    case 3: return pick_maxb<KF, HP, 3>(maxb);
+    case 4: return pick_maxb<KF, HP, 4>(maxb);
   }
-  const size_t idx_lds = ((size_t)L.ia.B + 1) * sizeof(int32_t);
-  const size_t att_lds = attn_lds_bytes(L.aa, kLayerWaves);
-  const size_t lds = idx_lds > att_lds ? idx_lds : att_lds;
-  return launch_kernel(kern, dim3(L.idx_wgs + items), dim3(64 * kLayerWaves), lds, s, L, tm);
+  return nullptr;
 }
 
 }  // namespace
 
 void set_layer_spin_limit(int polls) { g_spin_limit.store(polls, std::memory_order_relaxed); }
 
-hipError_t launch_layer_single(const IndexerArgs& ia, const AttnArgs& aa, uint32_t epoch, int key_format, int hp,
-                               hipStream_t s, const KTimer* tm) {
-  if (!ia.pooled || ia.scores || aa.pooled != ia.pooled || aa.splits != 1) return hipErrorInvalidValue;
+int layer_selectors(int max_blocks) { return (max_blocks + kSubBlocks - 1) / kSubBlocks; }
+
+hipError_t launch_layer_single(const IndexerArgs& ia, const AttnArgs& aa, const LayerScratch& ws, uint32_t epoch,
+                               bool fused, int key_format, int hp, hipStream_t s, const KTimer* tm) {
+  if (!ia.pooled || ia.scores || aa.pooled != ia.pooled || !ws.records || !ws.gave_up) return hipErrorInvalidValue;
+  if (aa.splits != 1 && aa.splits != 2 && aa.splits != 4) return hipErrorInvalidValue;
+  if (fused && aa.splits != 1) return hipErrorInvalidValue;
+  if (aa.splits > 1 && !ws.partials) return hipErrorInvalidValue;
   if (ia.B < 1 || ia.B > kIndexerMaxSeqs || ia.cus < 1) return hipErrorInvalidValue;
   if (aa.top_k < 1 || aa.top_k > kTopkMax || aa.maxb < 1 || aa.maxb > kSelectMaxBlocks) return hipErrorInvalidValue;
   if (aa.B != ia.B || aa.Tq != ia.Tq || aa.maxb != ia.maxb || aa.ctx_lens != ia.ctx_lens) return hipErrorInvalidValue;
-  const int64_t items = (int64_t)aa.B * aa.Tq * aa.Hkv;
+  if (aa.grp > 16 || aa.Tq < 1 || aa.Tq > 4) return hipErrorInvalidValue;
+  const int nsub = fused ? 0 : layer_selectors(aa.maxb);
+  if (nsub * kRecordWords > 7 * 64 || nsub * kTopkMax > 128) return hipErrorInvalidValue;
+  const int64_t tokens = (int64_t)aa.B * aa.Tq;
+  const int64_t work = fused ? tokens * aa.Hkv : tokens * (nsub + (int64_t)aa.Hkv * aa.splits);
   int64_t n_idx = (int64_t)kLayerWgsPerCu * ia.cus;
   const int64_t need = ((int64_t)ia.B * ia.maxb + 3) / 4;  // at least one block per wave
   if (n_idx > need) n_idx = need;
-  if (items < 1 || n_idx + items > INT32_MAX || n_idx > kLayerMaxIdxWgs) return hipErrorInvalidValue;
+  if (n_idx + work > INT32_MAX || n_idx > kLayerMaxIdxWgs) return hipErrorInvalidValue;
   const int limit = g_spin_limit.load(std::memory_order_relaxed);
-  LayerArgs L{ia, aa, (int)n_idx};
+  LayerArgs L{ia, aa, ws, (int)n_idx, nsub};
   L.aa.epoch = epoch;
   L.aa.spin_limit = limit > 0 ? limit : kSpinLimit;
+  const int maxb = kTopkMax / (kLayerWaves * aa.splits);  // blocks per wave at most
+  void* kern = nullptr;
   switch (key_format) {
-    case kKfFp8:
-      return hp == 8 ? launch_single_hp<kKfFp8, 8>(L, (int)items, s, tm) : launch_single_hp<kKfFp8, 4>(L, (int)items, s, tm);
-    case kKfNvfp4:
-      return hp == 8 ? launch_single_hp<kKfNvfp4, 8>(L, (int)items, s, tm)
-                     : launch_single_hp<kKfNvfp4, 4>(L, (int)items, s, tm);
-    default: return hipErrorInvalidValue;
+    case kKfFp8: kern = hp == 8 ? pick_tq<kKfFp8, 8>(aa.Tq, maxb) : pick_tq<kKfFp8, 4>(aa.Tq, maxb); break;
+    case kKfNvfp4: kern = hp == 8 ? pick_tq<kKfNvfp4, 8>(aa.Tq, maxb) : pick_tq<kKfNvfp4, 4>(aa.Tq, maxb); break;
   }
+  if (!kern) return hipErrorInvalidValue;
+  // dynamic LDS: the indexer's prefix sums, the selection's page table, the
+  // attention's V-scale stages, wave-merge slots and split states share one
+  // region
+  size_t lds = ((size_t)ia.B + 1) * sizeof(int32_t);
+  const size_t pages = (size_t)aa.maxb * sizeof(int32_t);
+  const size_t stage = (size_t)kLayerWaves * 1024 * 2;
+  const size_t merge = (size_t)(kLayerWaves - 1) * kSlotFloats * 4;
+  lds = lds > pages ? lds : pages;
+  lds = lds > stage ? lds : stage;
+  lds = lds > merge ? lds : merge;
+  return launch_kernel(reinterpret_cast<void (*)(LayerArgs)>(kern), dim3((unsigned)(n_idx + work)),
+                       dim3(kLayerThreads), lds, s, L, tm);
 }
 
 }  // namespace msa

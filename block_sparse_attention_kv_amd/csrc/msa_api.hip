@@ -8,6 +8,7 @@
 
 #include <atomic>
 #include <chrono>
+#include <mutex>
 
 #include "../../include/msa.h"
 #include "msa_internal.hpp"
@@ -97,15 +98,20 @@ msa_status_t check_cache_idx(const msa_params_t* p, const msa_cache_t* c) {
   return MSA_OK;
 }
 
-// Workspace: the pooled block scores of the two-kernel layer (fp32), those
-// of the single-launch layer (tagged 64-bit words, a region of their own so
-// that no fp32 pair the other layer left can pass for a tagged word) and, for
-// small batches whose attention items are split over several workgroups,
-// the per-split softmax states and one arrival word per item.
+// Workspace: the pooled block scores of the two-kernel layer (fp32); the
+// single-launch layer's tagged 64-bit words (pooled scores in a region of
+// their own, so that no fp32 pair the other layer left can pass for a tagged
+// word; the selection records; the split items' softmax states; the give-up
+// word); and, for small bf16 batches whose two-kernel attention items are
+// split over several workgroups, the per-split softmax states and one
+// arrival word per item.
 struct Layout {
-  size_t pooled_off, tagged_off, part_off, arrive_off, total;
+  size_t pooled_off, tagged_off, records_off, lpart_off, gave_up_off, part_off, arrive_off, total;
   int splits;
 };
+// Most workgroups per item the single launch uses: its split-state region is
+// sized for this, whatever the device.
+constexpr int kLayerMaxSplits = 4;
 // Only the bf16 path splits: its block loop has no prefetch, so a wave pays
 // the full load latency per block and one block per wave halves the chain.
 // The NVFP4 path prefetches the next block, and there the repeated fused
@@ -122,11 +128,27 @@ Layout layout(const msa_params_t* p) {
   L.splits = attn_splits(p);
   L.pooled_off = 0;
   L.tagged_off = align256(bt * p->max_blocks_per_seq * sizeof(float));
-  L.part_off = L.tagged_off + align256(bt * p->max_blocks_per_seq * sizeof(uint64_t));
+  L.records_off = L.tagged_off + align256(bt * p->max_blocks_per_seq * sizeof(uint64_t));
+  L.lpart_off = L.records_off + align256(bt * layer_selectors(p->max_blocks_per_seq) * kRecordWords * sizeof(uint64_t));
+  L.gave_up_off = L.lpart_off + align256(items * (kLayerMaxSplits - 1) * 16 * kPartRow * sizeof(uint64_t));
+  L.part_off = L.gave_up_off + 256;
   const size_t part = L.splits > 1 ? items * L.splits * 16 * kPartRow * sizeof(float) : 0;
   L.arrive_off = L.part_off + align256(part);
   L.total = L.arrive_off + (L.splits > 1 ? align256(items * sizeof(unsigned long long)) : 0);
   return L;
+}
+
+// Whether `s` is being captured into a HIP graph. The single launch and the
+// split attention tag their data with a per-call epoch that the host draws
+// at the call; a captured call would replay one epoch and take the previous
+// replay's words for its own. (A failed query counts as capturing.)
+bool capturing(hipStream_t s) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &cs) != hipSuccess) {
+    (void)hipGetLastError();
+    return true;
+  }
+  return cs != hipStreamCaptureStatusNone;
 }
 
 // A distinct epoch per attention launch (arrival words of older launches
@@ -141,20 +163,72 @@ uint32_t next_epoch() {
   }
 }
 
-// Splits the attention of small batches when the workspace has room.
-void set_splits(AttnArgs& a, const msa_params_t* p, void* workspace, size_t ws_bytes) {
+// Splits the two-kernel attention of small bf16 batches when the workspace
+// has room and the stream is not being captured.
+void set_splits(AttnArgs& a, const msa_params_t* p, void* workspace, size_t ws_bytes, hipStream_t s) {
   const Layout L = layout(p);
   a.splits = 1;
   a.partials = nullptr;
   a.arrivals = nullptr;
   a.epoch = 0;
-  if (L.splits > 1 && workspace && ws_bytes >= L.total && (reinterpret_cast<uintptr_t>(workspace) & 255) == 0) {
+  if (L.splits > 1 && workspace && ws_bytes >= L.total && (reinterpret_cast<uintptr_t>(workspace) & 255) == 0 &&
+      !capturing(s)) {
     uint8_t* ws = static_cast<uint8_t*>(workspace);
     a.splits = L.splits;
     a.partials = reinterpret_cast<float*>(ws + L.part_off);
     a.arrivals = reinterpret_cast<unsigned long long*>(ws + L.arrive_off);
     a.epoch = next_epoch();
   }
+}
+
+// The epoch of the latest single-launch call on each of the last few
+// workspaces (for msa_decode_layer_gave_up).
+struct EpochSlot {
+  const void* ws;
+  uint32_t epoch;
+};
+std::mutex g_epoch_mu;
+EpochSlot g_epochs[64];
+int g_epoch_next = 0;
+
+void remember_epoch(const void* ws, uint32_t e) {
+  std::lock_guard<std::mutex> lk(g_epoch_mu);
+  for (EpochSlot& sl : g_epochs)
+    if (sl.ws == ws) {
+      sl.epoch = e;
+      return;
+    }
+  g_epochs[g_epoch_next] = EpochSlot{ws, e};
+  g_epoch_next = (g_epoch_next + 1) % 64;
+}
+
+bool recalled_epoch(const void* ws, uint32_t* e) {
+  std::lock_guard<std::mutex> lk(g_epoch_mu);
+  for (const EpochSlot& sl : g_epochs)
+    if (sl.ws == ws && ws) {
+      *e = sl.epoch;
+      return true;
+    }
+  return false;
+}
+
+// Shape of the single launch. With at least one (sequence, token, KV head)
+// item per compute unit, or contexts of at most 1,024 blocks, one workgroup
+// per item selects and attends (fused). With fewer items over longer
+// contexts, a selection by one workgroup (four waves over thousands of
+// blocks) and a lone item per compute unit streaming four blocks per wave
+// leave the chip idle: per token, selectors over 1,024-block ranges, and
+// each item split over 4 workgroups of one block per wave. A debug export
+// can force the shape: 1 = fused, 2 or 4 = split with that many workgroups
+// per item.
+constexpr int kSplitMinBlocks = 1024;
+std::atomic<int> g_layer_splits{0};
+int device_cus();
+int layer_splits(const msa_params_t* p) {
+  const int forced = g_layer_splits.load(std::memory_order_relaxed);
+  if (forced > 0) return forced;
+  const int64_t items = (int64_t)p->num_seqs * p->q_len * p->num_kv_heads;
+  return (items >= (int64_t)device_cus() || p->max_blocks_per_seq <= kSplitMinBlocks) ? 1 : 4;
 }
 
 // Compute units of the current device (the persistent indexer grid is sized
@@ -314,7 +388,7 @@ msa_status_t msa_sparse_attn_decode(const msa_params_t* p, const msa_cache_t* c,
   if ((st = check_cache_kv(p, c)) != MSA_OK) return st;
   if (!q || !sel || !out) return fail(MSA_ERR_INVALID_ARG, "q / sel / out is NULL");
   AttnArgs a = attn_args(p, c, q, nullptr, const_cast<int32_t*>(sel), out, lse);
-  set_splits(a, p, workspace, ws_bytes);
+  set_splits(a, p, workspace, ws_bytes, static_cast<hipStream_t>(stream));
   hipError_t e = launch_attn(a, p->kv_dtype == MSA_KV_NVFP4, attn_waves(p), static_cast<hipStream_t>(stream));
   return e == hipSuccess ? MSA_OK : hip_fail(e, "attention launch");
 }
@@ -345,7 +419,7 @@ msa_status_t msa_decode_layer_traced(const msa_params_t* p, const msa_cache_t* c
 
   // selection (from the pooled scores) fused into the attention kernel
   AttnArgs aa = attn_args(p, c, q, pooled, sel_out, out, lse);
-  set_splits(aa, p, workspace, ws_bytes);
+  set_splits(aa, p, workspace, ws_bytes, s);
   e = launch_attn(aa, p->kv_dtype == MSA_KV_NVFP4, attn_waves(p), s, &t1);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   return MSA_OK;
@@ -375,16 +449,49 @@ msa_status_t msa_decode_layer_single_traced(const msa_params_t* p, const msa_cac
   if (ws_bytes < L.total) return fail(MSA_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, L.total);
   if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
     return fail(MSA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (capturing(s))
+    return fail(MSA_ERR_UNSUPPORTED, "single-launch layer: the stream is being captured into a graph (its data "
+                                     "carry a per-call tag drawn on the host, which a replay would repeat)");
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   float* pooled = reinterpret_cast<float*>(ws + L.tagged_off);  // tagged 64-bit words
   IndexerArgs ia = indexer_args(p, c, idx_q, idx_w);
   ia.pooled = pooled;
   AttnArgs aa = attn_args(p, c, q, pooled, sel_out, out, lse);
-  set_splits(aa, p, nullptr, 0);  // one workgroup per item
+  aa.splits = layer_splits(p);
+  if (aa.splits > kLayerMaxSplits) return fail(MSA_ERR_UNSUPPORTED, "%d workgroups per item", aa.splits);
+  LayerScratch sc;
+  sc.records = reinterpret_cast<uint64_t*>(ws + L.records_off);
+  sc.partials = reinterpret_cast<uint64_t*>(ws + L.lpart_off);
+  sc.gave_up = reinterpret_cast<unsigned long long*>(ws + L.gave_up_off);
+  const uint32_t epoch = next_epoch();
+  remember_epoch(workspace, epoch);
   const KTimer tm = stage_timer(ev, 0);
-  hipError_t e = launch_layer_single(ia, aa, next_epoch(), p->idx_dtype, p->idx_heads <= 4 ? 4 : 8,
-                                     static_cast<hipStream_t>(stream), &tm);
+  hipError_t e = launch_layer_single(ia, aa, sc, epoch, aa.splits == 1, p->idx_dtype, p->idx_heads <= 4 ? 4 : 8, s,
+                                     &tm);
   return e == hipSuccess ? MSA_OK : hip_fail(e, "single-launch layer");
+}
+
+msa_status_t msa_decode_layer_gave_up(const msa_params_t* p, const void* workspace, size_t ws_bytes, void* stream,
+                                      int64_t* count) {
+  g_err[0] = 0;
+  msa_status_t st = check_params(p);
+  if (st != MSA_OK) return st;
+  if (!count) return fail(MSA_ERR_INVALID_ARG, "count is NULL");
+  const Layout L = layout(p);
+  if (!workspace) return fail(MSA_ERR_WORKSPACE, "workspace is NULL");
+  if (ws_bytes < L.total) return fail(MSA_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, L.total);
+  *count = 0;
+  uint32_t epoch = 0;
+  if (!recalled_epoch(workspace, &epoch)) return MSA_OK;  // no single-launch call on it from this process
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  unsigned long long word = 0;
+  hipError_t e = hipMemcpyAsync(&word, static_cast<const uint8_t*>(workspace) + L.gave_up_off, sizeof(word),
+                                hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "reading the give-up word");
+  if ((uint32_t)(word >> 32) == epoch) *count = (int64_t)(word & 0xFFFFFFFFull);
+  return MSA_OK;
 }
 
 msa_status_t msa_decode_layer_single(const msa_params_t* p, const msa_cache_t* c, const void* q, const void* idx_q,
@@ -451,6 +558,14 @@ msa_status_t msa_debug_layer_spin_limit(int32_t polls) {
   g_err[0] = 0;
   if (polls < 0) return fail(MSA_ERR_INVALID_ARG, "polls must be >= 0");
   set_layer_spin_limit(polls);
+  return MSA_OK;
+}
+
+msa_status_t msa_debug_layer_splits(int32_t splits) {
+  g_err[0] = 0;
+  if (splits != 0 && splits != 1 && splits != 2 && splits != 4)
+    return fail(MSA_ERR_INVALID_ARG, "splits must be 0 (automatic), 1, 2 or 4");
+  g_layer_splits.store(splits, std::memory_order_relaxed);
   return MSA_OK;
 }
 

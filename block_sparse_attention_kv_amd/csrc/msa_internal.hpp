@@ -104,11 +104,29 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t s);
 hipError_t launch_insert(const InsertArgs& a, hipStream_t s);
 hipError_t launch_attn(const AttnArgs& a, bool nvfp4, int waves, hipStream_t s, const KTimer* t = nullptr);
 // The decode layer as one launch (layer.hip); NVFP4 K/V, FP8 or NVFP4
-// indexer keys, q_len <= 4. ia.pooled / aa.pooled: the workspace's pooled
-// scores, 8 bytes per entry; epoch: distinct per call.
+// indexer keys, q_len <= 4. ia.pooled / aa.pooled: the workspace's tagged
+// pooled scores, 8 bytes per entry; aa.splits: workgroups per attention
+// item (1, 2 or 4); epoch: distinct per call, never 0.
 constexpr int kLayerMaxIdxWgs = 4096;
-hipError_t launch_layer_single(const IndexerArgs& ia, const AttnArgs& aa, uint32_t epoch, int key_format, int hp,
-                               hipStream_t s, const KTimer* t = nullptr);
+// Candidate record of one selector of the single launch (a range of at most
+// 1,024 blocks of one query token): a header word (count of candidates,
+// kRecordStale when the selection gave up) and three words per candidate
+// (ranking key, logical block, page); every word tagged with the call's
+// epoch. Padded to kRecordWords words.
+constexpr int kRecordWords = 56;
+constexpr uint32_t kRecordStale = 0x80000000u;
+struct LayerScratch {
+  uint64_t* records;            // [B * Tq][selectors][kRecordWords] (split shape)
+  uint64_t* partials;           // [items][splits - 1][16][kPartRow] tagged softmax states (splits > 1)
+  unsigned long long* gave_up;  // (epoch << 32) | workgroups of that call that gave up a wait
+};
+// Selectors per query token in the split shape for a block table of
+// max_blocks columns.
+int layer_selectors(int max_blocks);
+// fused: one workgroup per item selects and attends (aa.splits must be 1);
+// otherwise selectors plus aa.splits attention workgroups per item.
+hipError_t launch_layer_single(const IndexerArgs& ia, const AttnArgs& aa, const LayerScratch& ws, uint32_t epoch,
+                               bool fused, int key_format, int hp, hipStream_t s, const KTimer* t = nullptr);
 // Poll limit of the single-launch layer's waits for later launches (0: the
 // default of about a second).
 void set_layer_spin_limit(int polls);

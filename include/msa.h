@@ -169,7 +169,8 @@ size_t msa_workspace_size(const msa_params_t* p);
 
 /* Indexer: every key of every sequence is scored against the indexer query
  * of every query token [ainewsbites page, section "A model built for
- * efficient inference": "scores every key in the context"].
+ * efficient inference": the indexer gives a score to each key of the whole
+ * context].
  *   idx_q  device bf16[B][q_len][idx_heads][64]
  *   idx_w  device f32 [B][q_len][idx_heads]   head weights
  *   scores device f32 [B][q_len][max_blocks_per_seq*128]: s[b,t,j] for
@@ -196,8 +197,8 @@ msa_status_t msa_pool_select_blocks(const msa_params_t* p, const int32_t* ctx_le
                                     int32_t* nsel, void* stream);
 
 /* Exact attention of every query head over the keys of the selected blocks
- * [same section: "Main attention then runs exactly, but only over the top 16
- * blocks"], keys j <= p_t only, K/V dequantised inside the kernel.
+ * [same section: the attention itself is exact, restricted to the 16 best
+ * blocks], keys j <= p_t only, K/V dequantised inside the kernel.
  *   q     device bf16[B][q_len][num_q_heads][128]
  *   sel   device i32[B][q_len][top_k] (as produced by msa_pool_select_blocks;
  *         entries < 0 or >= max_blocks_per_seq are skipped)
@@ -239,30 +240,48 @@ msa_status_t msa_decode_layer_traced(const msa_params_t* p, const msa_cache_t* c
 /* msa_decode_layer as ONE kernel launch on `stream` [upstreambeat page
  * "vLLM turns MiniMax's day-zero promise into GPU-specific serving code",
  * section "What changed": a single-launch ("mono") decode path on MI355X to
- * cut launch overhead]: the first workgroups of the grid run the indexer
- * and pooling phase and publish every pooled score tagged with the call's
- * epoch; the others, one per (sequence, token, KV head), each wait for the
- * tagged scores of their query token, then select and attend. Same
- * arguments, workspace and selection as msa_decode_layer; its attention
- * always runs 4 waves per (sequence, token, KV head), so out and lse equal
- * msa_decode_layer's bit for bit when the batch has at least two such items
- * per compute unit (below that, msa_decode_layer spreads an item over 8
- * waves and the rounding of the merge differs). Attention workgroups are
- * dispatched after every indexer workgroup and indexer workgroups wait on
- * nothing, so every wait ends; each wait is also bounded (see
- * msa_debug_layer_spin_limit). Supported: kv_dtype MSA_KV_NVFP4, idx_dtype
- * MSA_IDX_FP8_E4M3 or MSA_IDX_NVFP4, q_len <= 4; other valid problems return
- * MSA_ERR_UNSUPPORTED before anything is enqueued. Workspace: the tagged
- * scores sit in a region of their own, and a word counts only when its tag
- * equals the call's epoch (a per-call 32-bit value, never 0). Words the
- * library wrote in earlier calls never match; memory it never wrote matches
- * with probability about 2^-32 per word, so a workspace should be
- * zero-filled once before its first use (the Python binding's
- * alloc_workspace does) — no clearing is needed between calls. */
+ * cut launch overhead]. The grid runs, in dispatch order, the indexer and
+ * pooling phase, which publishes every pooled score tagged with the call's
+ * epoch, then the selection and attention. With at least one (sequence,
+ * token, KV head) item per compute unit, one workgroup per item reads its
+ * token's tagged scores, selects and attends. With fewer items, each token
+ * gets selector workgroups (one per 1,024 blocks of max_blocks_per_seq)
+ * that publish their top-k candidates as tagged records, and each item is
+ * split over 4 attention workgroups that merge the candidates, attend to a
+ * share of the selected blocks and meet through tagged partial softmax
+ * states, the last one merging them in a fixed order, so results do not
+ * depend on timing. Same arguments, workspace and selection as
+ * msa_decode_layer; out and lse equal msa_decode_layer's bit for bit from
+ * two items per compute unit up (below that the two paths merge partial
+ * states in different orders and agree to rounding). Every wait is on a
+ * workgroup dispatched earlier and the indexer workgroups wait on nothing,
+ * so every wait ends; each wait is also bounded (see
+ * msa_debug_layer_spin_limit): a workgroup that gives up marks its results
+ * invalid (NaN out and lse, selection -1 when the selection itself gave up)
+ * and is counted in the workspace (msa_decode_layer_gave_up).
+ * Supported: kv_dtype MSA_KV_NVFP4, idx_dtype MSA_IDX_FP8_E4M3 or
+ * MSA_IDX_NVFP4, q_len <= 4, and a stream that is not being captured into a
+ * HIP graph (the call's epoch is drawn on the host, and a replayed graph
+ * would repeat it); anything else returns MSA_ERR_UNSUPPORTED before
+ * anything is enqueued. Workspace: a word counts only when its tag equals the
+ * call's epoch (a per-call 32-bit value, never 0). Words the library wrote in
+ * earlier calls never match; memory it never wrote matches with probability
+ * about 2^-32 per word, so a workspace should be zero-filled once before its
+ * first use (the Python binding's alloc_workspace does) -- no clearing is
+ * needed between calls. */
 msa_status_t msa_decode_layer_single(const msa_params_t* p, const msa_cache_t* cache,
                                      const void* q, const void* idx_q, const float* idx_w,
                                      void* out, float* lse, int32_t* sel_out,
                                      void* workspace, size_t ws_bytes, void* stream);
+
+/* The number of workgroups of the latest msa_decode_layer_single call made
+ * on `workspace` by this process that gave up a bounded wait, written to
+ * *count (0: the call's results are complete; otherwise the affected rows
+ * hold NaN). Reads one word of the workspace with a copy on `stream` and
+ * synchronises `stream`. A workspace no single-launch call of this process
+ * has used gives 0. p: the parameters the workspace was sized for. */
+msa_status_t msa_decode_layer_gave_up(const msa_params_t* p, const void* workspace, size_t ws_bytes,
+                                      void* stream, int64_t* count);
 
 /* msa_decode_layer_single with a tracing hook: when `events` is not NULL it
  * holds 2 hipEvent_t handles (NULL entries allowed) into which the kernel's
@@ -337,6 +356,13 @@ msa_status_t msa_debug_read_bandwidth(const void* buf, int64_t bytes, uint32_t* 
  * process; polls < 0 returns MSA_ERR_INVALID_ARG. For tests of the bounded
  * wait. */
 msa_status_t msa_debug_layer_spin_limit(int32_t polls);
+
+/* Debug export: the shape of later msa_decode_layer_single calls in this
+ * process: 1 = one workgroup per item (fused selection), 2 or 4 = selectors
+ * plus that many attention workgroups per item; 0 restores the automatic
+ * choice. For measurements and tests of each shape. Other values return
+ * MSA_ERR_INVALID_ARG. */
+msa_status_t msa_debug_layer_splits(int32_t splits);
 
 /* Human-readable name of a status code (static string). */
 const char* msa_status_string(msa_status_t s);

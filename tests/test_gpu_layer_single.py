@@ -1,18 +1,22 @@
-"""GPU parity of msa_decode_layer_single (one cooperative launch) through the
-C ABI: against the oracle on small ragged batches and on sampled tokens of
-the full-size configurations (tolerances of tests/gpu_util.py), and against
-msa_decode_layer, whose kernels run the same device code: the same selection
-everywhere, and the same output bits where both run the attention with 4
-waves per item (the full-size 128K speculative-verify batch of 32 sequences
-x 4 tokens, and a batch with more (sequence, token, KV head) items than the
-grid has workgroups)."""
+"""GPU parity of msa_decode_layer_single (one launch) through the C ABI:
+against the oracle on small ragged batches, every split of the attention
+items, edge contexts, scales and selection variants (tolerances of
+tests/gpu_util.py; the full-size workloads are in test_gpu_configs.py), and
+against msa_decode_layer, whose kernels run the same device code: the same
+selection everywhere, and the same output bits where both run the attention
+with 4 waves and one workgroup per item (batches with at least two items
+per compute unit). Also its bounded waits, the give-up query and graph
+capture."""
+import contextlib
+import gc
+
 import numpy as np
 import pytest
 import torch
 
 import block_sparse_attention_kv_amd as msa
 from tests import gpu_util as G
-from workloads import make_workload, make_config, KV_NVFP4, KV_BF16, IDX_FP8, IDX_NVFP4, IDX_BF16
+from workloads import make_workload, make_config, small_cases, KV_NVFP4, KV_BF16, IDX_FP8, IDX_NVFP4, IDX_BF16
 
 pytestmark = pytest.mark.gpu
 
@@ -174,43 +178,183 @@ def test_single_traced_matches_plain():
     assert np.array_equal(sel.cpu().numpy(), want["sel"])
 
 
-def test_single_bounded_wait_gives_up_cleanly():
-    # With a poll limit of 1 an attention workgroup that finds its indexer
-    # workgroups unfinished at the first poll gives up at once: the kernel
-    # still ends, every item is either the normal result or marked invalid
-    # (NaN output and lse, selection -1), and the default limit restores the
-    # normal result on the next call.
+@pytest.mark.parametrize("shape", [0, 1])
+def test_single_bounded_wait_gives_up_cleanly(shape):
+    # With a poll limit of 1 a workgroup that finds the data it waits for
+    # unpublished at the first poll gives up at once: the kernel still ends,
+    # every (token, KV head) item is either the normal result or marked
+    # invalid (NaN output and lse; the token's selection either the normal
+    # one or all -1 when the workgroup writing it gave up), the give-up
+    # query counts the workgroups
+    # that stopped, and the default limit restores the normal result (and a
+    # zero count) on the next call.
     w = make_workload("single_spin", 69, [20000] * 24, 4, 16, 2, 8, KV_NVFP4, IDX_FP8, table="permute")
     run = G.Run(w)
-    want = run.layer(single=True)
-    try:
-        msa.msa_debug_layer_spin_limit(1)
-        got = run.layer(single=True)
-    finally:
-        msa.msa_debug_layer_spin_limit(0)
     prm = w.params
     B, Tq, Hkv, grp = prm["num_seqs"], prm["q_len"], prm["num_kv_heads"], prm["num_q_heads"] // prm["num_kv_heads"]
-    gave_up = 0
+    Hq, K = prm["num_q_heads"], prm["top_k"]
+    ws = msa.alloc_workspace(run.params, "cuda")
+
+    def call():
+        out = torch.empty((B, Tq, Hq, 128), dtype=torch.int16, device="cuda")
+        lse = torch.empty((B, Tq, Hq), dtype=torch.float32, device="cuda")
+        sel = torch.empty((B, Tq, K), dtype=torch.int32, device="cuda")
+        msa.msa_decode_layer_single(run.params, run.cache, run.q, run.idx_q, run.idx_w, out, ws, lse=lse, sel_out=sel)
+        torch.cuda.synchronize()
+        return out.cpu().numpy(), lse.cpu().numpy(), sel.cpu().numpy()
+
+    msa.msa_debug_layer_splits(shape)  # 0: the automatic shape (split, for these 192 items); 1: fused
+    try:
+        want = call()
+        assert msa.msa_decode_layer_gave_up(run.params, ws) == 0
+        try:
+            msa.msa_debug_layer_spin_limit(1)
+            got = call()
+        finally:
+            msa.msa_debug_layer_spin_limit(0)
+    finally:
+        msa.msa_debug_layer_splits(0)
+    n_gave_up = msa.msa_decode_layer_gave_up(run.params, ws)
+    invalid = 0
     for b in range(B):
         for t in range(Tq):
+            sel_ok = np.array_equal(got[2][b, t], want[2][b, t])
+            assert sel_ok or np.all(got[2][b, t] == -1), (b, t)
             for g in range(Hkv):
                 heads = slice(g * grp, (g + 1) * grp)
-                o = got["out_bits"][b, t, heads]
+                o = got[0][b, t, heads]
                 if np.all(o.view(np.uint16) == 0x7FC0):
-                    assert np.all(np.isnan(got["lse"][b, t, heads]))
-                    if g == 0:
-                        assert np.all(got["sel"][b, t] == -1)
-                    gave_up += 1
+                    assert np.all(np.isnan(got[1][b, t, heads]))
+                    invalid += 1
                 else:
-                    assert np.array_equal(o, want["out_bits"][b, t, heads]), (b, t, g)
-                    if g == 0:
-                        assert np.array_equal(got["sel"][b, t], want["sel"][b, t]), (b, t)
-                    assert np.array_equal(got["lse"][b, t, heads].view(np.uint64),
-                                          want["lse"][b, t, heads].view(np.uint64)), (b, t, g)
-    print("items that gave up with a poll limit of 1: %d of %d" % (gave_up, B * Tq * Hkv))
-    again = run.layer(single=True)
-    assert np.array_equal(again["out_bits"], want["out_bits"])
-    assert np.array_equal(again["sel"], want["sel"])
+                    assert np.array_equal(o, want[0][b, t, heads]), (b, t, g)
+                    assert np.array_equal(got[1][b, t, heads].view(np.uint32),
+                                          want[1][b, t, heads].view(np.uint32)), (b, t, g)
+    print("with a poll limit of 1: %d of %d items invalid, %d workgroups gave up" % (invalid, B * Tq * Hkv, n_gave_up))
+    assert (invalid > 0) == (n_gave_up > 0)
+    msa.msa_debug_layer_splits(shape)
+    try:
+        again = call()
+    finally:
+        msa.msa_debug_layer_splits(0)
+    assert msa.msa_decode_layer_gave_up(run.params, ws) == 0
+    for g_, w_ in zip(again, want):
+        assert np.array_equal(g_.view(np.uint8), w_.view(np.uint8))
+
+
+@pytest.mark.parametrize("splits", [1, 2, 4])
+def test_single_forced_splits(splits):
+    # every split count on batches whose automatic choice differs: against
+    # the oracle, and deterministic over repeated calls
+    w = make_workload("single_split%d" % splits, 74, [5000, 129, 2100, 300, 40000], 4, 16, 2, 8, KV_NVFP4, IDX_FP8,
+                      table="pool", pool_factor=1.2, n_planted=3)
+    run = G.Run(w)
+    try:
+        msa.msa_debug_layer_splits(splits)
+        first = run.layer(single=True)
+        again = run.layer(single=True)
+        ties, mx, mean = G.layer_parity(w, run=run, single=True)
+    finally:
+        msa.msa_debug_layer_splits(0)
+    assert np.array_equal(first["out_bits"], again["out_bits"])
+    assert np.array_equal(first["lse"].view(np.uint64), again["lse"].view(np.uint64))
+    assert np.array_equal(first["sel"], again["sel"])
+    print("splits %d: ties %d, out max-abs %.2e mean-abs %.2e" % (splits, ties, mx, mean))
+
+
+def test_single_split_counts_agree_on_selection():
+    # the selection does not depend on how the attention is split; the
+    # outputs agree to rounding
+    w = make_workload("single_split_sel", 75, [9000, 3000], 4, 32, 4, 8, KV_NVFP4, IDX_NVFP4, table="permute")
+    run = G.Run(w)
+    res = {}
+    try:
+        for s in (1, 2, 4):
+            msa.msa_debug_layer_splits(s)
+            res[s] = run.layer(single=True)
+    finally:
+        msa.msa_debug_layer_splits(0)
+    for s in (2, 4):
+        assert np.array_equal(res[s]["sel"], res[1]["sel"])
+        assert np.max(np.abs(res[s]["out"] - res[1]["out"])) <= 2 * G.OUT_MAX_ABS
+
+
+@contextlib.contextmanager
+def _no_gc_capture():
+    """Objects left by earlier tests (tensors, graphs) must not be destroyed
+    while a stream is being captured: their destructors make HIP calls that a
+    capture does not permit, and HIP aborts the process. Collect them first
+    and keep the collector off during the capture."""
+    gc.collect()
+    torch.cuda.synchronize()
+    gc.disable()
+    try:
+        yield
+    finally:
+        gc.enable()
+
+
+def test_single_rejects_graph_capture():
+    # the call's epoch is drawn on the host: a captured launch would replay
+    # it, so the single launch refuses to be captured (before enqueueing)
+    w = make_workload("single_capture", 76, [3000, 700], 4, 16, 2, 8, KV_NVFP4, IDX_FP8, table="permute")
+    run = G.Run(w)
+    prm = w.params
+    B, Tq, Hq = prm["num_seqs"], prm["q_len"], prm["num_q_heads"]
+    out = torch.empty((B, Tq, Hq, 128), dtype=torch.int16, device="cuda")
+    ws = msa.alloc_workspace(run.params, "cuda")
+    graph = torch.cuda.CUDAGraph()
+    err = None
+    with _no_gc_capture():
+        try:
+            with torch.cuda.graph(graph):
+                try:
+                    msa.msa_decode_layer_single(run.params, run.cache, run.q, run.idx_q, run.idx_w, out, ws)
+                except msa.MSAError as e:
+                    err = e
+        except RuntimeError:
+            pass  # an empty capture may be refused by torch; the library's answer is what is checked
+    torch.cuda.synchronize()
+    # the refused graph is released here, outside any capture: its destructor
+    # makes HIP calls that a capture in progress would not permit
+    del graph
+    gc.collect()
+    assert err is not None and err.status == msa.MSA_ERR_UNSUPPORTED, err
+    # and the next uncaptured call works
+    G.layer_parity(w, run=run, single=True)
+
+
+def test_two_kernel_layer_graph_replays():
+    # msa_decode_layer needs no per-call tag when its stream is captured (the
+    # split bf16 attention falls back to one workgroup per item): a captured
+    # step replays correctly, with eager work and synchronisations between
+    # the replays, and every replay matches the oracle
+    w = small_cases()[1]                              # bf16 cache: split attention when eager
+    run = G.Run(w)
+    prm = w.params
+    B, Tq, Hq, K = prm["num_seqs"], prm["q_len"], prm["num_q_heads"], prm["top_k"]
+    out = torch.zeros((B, Tq, Hq, 128), dtype=torch.int16, device="cuda")
+    lse = torch.zeros((B, Tq, Hq), dtype=torch.float32, device="cuda")
+    sel = torch.zeros((B, Tq, K), dtype=torch.int32, device="cuda")
+    ws = msa.alloc_workspace(run.params, "cuda")
+    msa.msa_decode_layer(run.params, run.cache, run.q, run.idx_q, run.idx_w, out, ws, lse=lse, sel_out=sel)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with _no_gc_capture():
+        with torch.cuda.graph(graph):
+            msa.msa_decode_layer(run.params, run.cache, run.q, run.idx_q, run.idx_w, out, ws, lse=lse, sel_out=sel)
+    torch.cuda.synchronize()
+    refs = G.oracle_refs(w)
+    for i in range(3):
+        out.zero_()
+        lse.zero_()
+        sel.fill_(7)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        res = dict(out=G.bf16_to_np(out), out_bits=out.cpu().numpy(), lse=lse.cpu().numpy().astype(np.float64),
+                   sel=sel.cpu().numpy())
+        G.compare_layer(w, res, refs, label="%s replay %d" % (w.name, i))
 
 
 def test_single_spin_limit_rejects_negative():

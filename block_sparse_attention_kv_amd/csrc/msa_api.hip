@@ -330,6 +330,52 @@ KTimer stage_timer(void* const* ev, int i) {
   return t;
 }
 
+// Host-visible checks of the single-launch entries.
+msa_status_t check_single(const msa_params_t* p, const msa_cache_t* c, const void* q, const void* idx_q,
+                          const float* idx_w, void* out) {
+  msa_status_t st = check_params(p);
+  if (st != MSA_OK) return st;
+  if (p->kv_dtype != MSA_KV_NVFP4 || (p->idx_dtype != MSA_IDX_FP8_E4M3 && p->idx_dtype != MSA_IDX_NVFP4) ||
+      p->q_len > 4)
+    return fail(MSA_ERR_UNSUPPORTED, "single-launch layer: NVFP4 K/V, FP8 or NVFP4 indexer keys, q_len <= 4");
+  if ((st = check_cache_kv(p, c)) != MSA_OK) return st;
+  if ((st = check_cache_idx(p, c)) != MSA_OK) return st;
+  if (!q || !idx_q || !idx_w || !out) return fail(MSA_ERR_INVALID_ARG, "q / idx_q / idx_w / out is NULL");
+  return MSA_OK;
+}
+
+// Device scratch of one single-launch call: the tagged pooled scores, the
+// selection records, the split items' states, the give-up word.
+struct SingleScratch {
+  uint8_t *tagged, *records, *partials, *gave_up;
+};
+
+// The single launch on scratch `sc`; `owner` identifies the scratch for
+// msa_decode_layer_gave_up.
+msa_status_t run_single(const msa_params_t* p, const msa_cache_t* c, const void* q, const void* idx_q,
+                        const float* idx_w, void* out, float* lse, int32_t* sel_out, const SingleScratch& sc,
+                        const void* owner, hipStream_t s, void* const* ev) {
+  if (capturing(s))
+    return fail(MSA_ERR_UNSUPPORTED, "single-launch layer: the stream is being captured into a graph (its data "
+                                     "carry a per-call tag drawn on the host, which a replay would repeat)");
+  float* pooled = reinterpret_cast<float*>(sc.tagged);  // tagged 64-bit words
+  IndexerArgs ia = indexer_args(p, c, idx_q, idx_w);
+  ia.pooled = pooled;
+  AttnArgs aa = attn_args(p, c, q, pooled, sel_out, out, lse);
+  aa.splits = layer_splits(p);
+  if (aa.splits > kLayerMaxSplits) return fail(MSA_ERR_UNSUPPORTED, "%d workgroups per item", aa.splits);
+  LayerScratch ls;
+  ls.records = reinterpret_cast<uint64_t*>(sc.records);
+  ls.partials = reinterpret_cast<uint64_t*>(sc.partials);
+  ls.gave_up = reinterpret_cast<unsigned long long*>(sc.gave_up);
+  const uint32_t epoch = next_epoch();
+  remember_epoch(owner, epoch);
+  const KTimer tm = stage_timer(ev, 0);
+  hipError_t e = launch_layer_single(ia, aa, ls, epoch, aa.splits == 1, p->idx_dtype, p->idx_heads <= 4 ? 4 : 8, s,
+                                     &tm);
+  return e == hipSuccess ? MSA_OK : hip_fail(e, "single-launch layer");
+}
+
 }  // namespace
 
 namespace msa {
@@ -436,40 +482,20 @@ msa_status_t msa_decode_layer_single_traced(const msa_params_t* p, const msa_cac
                                             int32_t* sel_out, void* workspace, size_t ws_bytes, void* stream,
                                             void* const* ev) {
   g_err[0] = 0;
-  msa_status_t st = check_params(p);
+  msa_status_t st = check_single(p, c, q, idx_q, idx_w, out);
   if (st != MSA_OK) return st;
-  if (p->kv_dtype != MSA_KV_NVFP4 || (p->idx_dtype != MSA_IDX_FP8_E4M3 && p->idx_dtype != MSA_IDX_NVFP4) ||
-      p->q_len > 4)
-    return fail(MSA_ERR_UNSUPPORTED, "single-launch layer: NVFP4 K/V, FP8 or NVFP4 indexer keys, q_len <= 4");
-  if ((st = check_cache_kv(p, c)) != MSA_OK) return st;
-  if ((st = check_cache_idx(p, c)) != MSA_OK) return st;
-  if (!q || !idx_q || !idx_w || !out) return fail(MSA_ERR_INVALID_ARG, "q / idx_q / idx_w / out is NULL");
   const Layout L = layout(p);
   if (!workspace) return fail(MSA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", L.total);
   if (ws_bytes < L.total) return fail(MSA_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, L.total);
   if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
     return fail(MSA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if (capturing(s))
-    return fail(MSA_ERR_UNSUPPORTED, "single-launch layer: the stream is being captured into a graph (its data "
-                                     "carry a per-call tag drawn on the host, which a replay would repeat)");
   uint8_t* ws = static_cast<uint8_t*>(workspace);
-  float* pooled = reinterpret_cast<float*>(ws + L.tagged_off);  // tagged 64-bit words
-  IndexerArgs ia = indexer_args(p, c, idx_q, idx_w);
-  ia.pooled = pooled;
-  AttnArgs aa = attn_args(p, c, q, pooled, sel_out, out, lse);
-  aa.splits = layer_splits(p);
-  if (aa.splits > kLayerMaxSplits) return fail(MSA_ERR_UNSUPPORTED, "%d workgroups per item", aa.splits);
-  LayerScratch sc;
-  sc.records = reinterpret_cast<uint64_t*>(ws + L.records_off);
-  sc.partials = reinterpret_cast<uint64_t*>(ws + L.lpart_off);
-  sc.gave_up = reinterpret_cast<unsigned long long*>(ws + L.gave_up_off);
-  const uint32_t epoch = next_epoch();
-  remember_epoch(workspace, epoch);
-  const KTimer tm = stage_timer(ev, 0);
-  hipError_t e = launch_layer_single(ia, aa, sc, epoch, aa.splits == 1, p->idx_dtype, p->idx_heads <= 4 ? 4 : 8, s,
-                                     &tm);
-  return e == hipSuccess ? MSA_OK : hip_fail(e, "single-launch layer");
+  SingleScratch sc;
+  sc.tagged = ws + L.tagged_off;
+  sc.records = ws + L.records_off;
+  sc.partials = ws + L.lpart_off;
+  sc.gave_up = ws + L.gave_up_off;
+  return run_single(p, c, q, idx_q, idx_w, out, lse, sel_out, sc, workspace, static_cast<hipStream_t>(stream), ev);
 }
 
 msa_status_t msa_decode_layer_gave_up(const msa_params_t* p, const void* workspace, size_t ws_bytes, void* stream,

@@ -80,6 +80,7 @@ def load():
         "msa_decode_layer_traced": (st, [P, C, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp]),
         "msa_decode_layer_single": (st, [P, C, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
         "msa_decode_layer_single_traced": (st, [P, C, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp]),
+        "msa_decode_layer_single_static": (st, [P, C, vp, vp, vp, vp, vp, vp, vp]),
         "msa_kv_insert": (st, [P, C, vp, vp, vp, vp]),
         "msa_debug_dequant_nvfp4": (st, [vp, vp, i64, vp, vp]),
         "msa_debug_dequant_fp8": (st, [vp, i64, vp, vp]),
@@ -101,7 +102,7 @@ def load():
 
 EXPORTED = ("msa_workspace_size", "msa_indexer_scores", "msa_pool_select_blocks", "msa_sparse_attn_decode",
             "msa_decode_layer", "msa_decode_layer_traced", "msa_decode_layer_single",
-            "msa_decode_layer_single_traced", "msa_kv_insert", "msa_debug_dequant_nvfp4",
+            "msa_decode_layer_single_traced", "msa_decode_layer_single_static", "msa_kv_insert", "msa_debug_dequant_nvfp4",
             "msa_debug_dequant_fp8", "msa_debug_read_bandwidth", "msa_debug_layer_spin_limit",
             "msa_debug_layer_splits", "msa_decode_layer_gave_up",
             "msa_status_string", "msa_last_error", "msa_version")
@@ -234,6 +235,15 @@ def msa_decode_layer_single(params, cache, q, idx_q, idx_w, out, workspace, lse=
     _check(load().msa_decode_layer_single(ctypes.byref(params), ctypes.byref(c), _ptr(q), _ptr(idx_q), _ptr(idx_w),
                                           _ptr(out), _ptr(lse), _ptr(sel_out), _ptr(workspace), ws_bytes,
                                           _stream(stream)), "msa_decode_layer_single")
+
+
+def msa_decode_layer_single_static(params, cache, q, idx_q, idx_w, out, lse=None, sel_out=None, stream=None):
+    """msa_decode_layer_single on the library's static per-GPU scratch: no
+    workspace, no allocation (calls that may overlap on one GPU race)."""
+    c = cache.c()
+    _check(load().msa_decode_layer_single_static(ctypes.byref(params), ctypes.byref(c), _ptr(q), _ptr(idx_q),
+                                                 _ptr(idx_w), _ptr(out), _ptr(lse), _ptr(sel_out), _stream(stream)),
+           "msa_decode_layer_single_static")
 
 
 def msa_kv_insert(params, cache, new_k, new_v, new_idx_k, stream=None):

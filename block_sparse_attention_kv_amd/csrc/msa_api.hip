@@ -15,6 +15,12 @@
 
 using namespace msa;
 
+// Scratch of msa_decode_layer_single_static: one array per GPU (the code
+// object's copy on each device), held until the process ends. Host code never
+// uses this name as an address: the device address comes from
+// hipGetSymbolAddress, once per device (static_scratch below).
+static __device__ __align__(256) uint8_t scratch[MSA_STATIC_SCRATCH_BYTES];
+
 namespace {
 
 thread_local char g_err[512] = "";
@@ -376,6 +382,43 @@ msa_status_t run_single(const msa_params_t* p, const msa_cache_t* c, const void*
   return e == hipSuccess ? MSA_OK : hip_fail(e, "single-launch layer");
 }
 
+// Offsets in the static scratch: the single launch's regions only, the
+// split states only for the shape that uses them.
+struct StaticLayout {
+  size_t tagged_off, records_off, lpart_off, gave_up_off, total;
+};
+StaticLayout static_layout(const msa_params_t* p, int splits) {
+  StaticLayout L;
+  const size_t bt = (size_t)p->num_seqs * p->q_len;
+  const size_t items = bt * p->num_kv_heads;
+  L.tagged_off = 0;
+  L.records_off = align256(bt * p->max_blocks_per_seq * sizeof(uint64_t));
+  L.lpart_off = L.records_off + align256(bt * layer_selectors(p->max_blocks_per_seq) * kRecordWords * sizeof(uint64_t));
+  L.gave_up_off = L.lpart_off + (splits > 1 ? align256(items * (splits - 1) * 16 * kPartRow * sizeof(uint64_t)) : 0);
+  L.total = L.gave_up_off + 256;
+  return L;
+}
+
+// Device address of the static scratch on the current device, looked up
+// once per device with that device current.
+std::mutex g_scratch_mu;
+uint8_t* g_scratch[64];
+msa_status_t static_scratch(uint8_t** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= 64) return fail(MSA_ERR_UNSUPPORTED, "device %d", dev);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) return hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol, "hipGetSymbolAddress(scratch)");
+    g_scratch[dev] = static_cast<uint8_t*>(ptr);
+  }
+  *out = g_scratch[dev];
+  return MSA_OK;
+}
+
 }  // namespace
 
 namespace msa {
@@ -496,6 +539,26 @@ msa_status_t msa_decode_layer_single_traced(const msa_params_t* p, const msa_cac
   sc.partials = ws + L.lpart_off;
   sc.gave_up = ws + L.gave_up_off;
   return run_single(p, c, q, idx_q, idx_w, out, lse, sel_out, sc, workspace, static_cast<hipStream_t>(stream), ev);
+}
+
+msa_status_t msa_decode_layer_single_static(const msa_params_t* p, const msa_cache_t* c, const void* q,
+                                            const void* idx_q, const float* idx_w, void* out, float* lse,
+                                            int32_t* sel_out, void* stream) {
+  g_err[0] = 0;
+  msa_status_t st = check_single(p, c, q, idx_q, idx_w, out);
+  if (st != MSA_OK) return st;
+  const StaticLayout L = static_layout(p, layer_splits(p));
+  if (L.total > (size_t)MSA_STATIC_SCRATCH_BYTES)
+    return fail(MSA_ERR_UNSUPPORTED, "static scratch: %zu bytes needed, the array holds %u (use "
+                                     "msa_decode_layer_single with a workspace)", L.total, MSA_STATIC_SCRATCH_BYTES);
+  uint8_t* base = nullptr;
+  if ((st = static_scratch(&base)) != MSA_OK) return st;
+  SingleScratch sc;
+  sc.tagged = base + L.tagged_off;
+  sc.records = base + L.records_off;
+  sc.partials = base + L.lpart_off;
+  sc.gave_up = base + L.gave_up_off;
+  return run_single(p, c, q, idx_q, idx_w, out, lse, sel_out, sc, base, static_cast<hipStream_t>(stream), nullptr);
 }
 
 msa_status_t msa_decode_layer_gave_up(const msa_params_t* p, const void* workspace, size_t ws_bytes, void* stream,

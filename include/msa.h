@@ -283,6 +283,30 @@ msa_status_t msa_decode_layer_single(const msa_params_t* p, const msa_cache_t* c
 msa_status_t msa_decode_layer_gave_up(const msa_params_t* p, const void* workspace, size_t ws_bytes,
                                       void* stream, int64_t* count);
 
+/* Bytes of device memory per GPU that msa_decode_layer_single_static uses as
+ * its scratch. */
+#define MSA_STATIC_SCRATCH_BYTES (32u << 20)
+
+/* msa_decode_layer_single without a workspace, for callers that cannot
+ * allocate device memory (tight serving loops, harnesses that forbid
+ * allocation). Its scratch (the tagged pooled scores, selection records and
+ * split states) is a fixed array of MSA_STATIC_SCRATCH_BYTES bytes in the
+ * library's code object, one per GPU, held until the process ends; the call
+ * itself allocates nothing. The caller still passes every input and output;
+ * arguments, results and limits are msa_decode_layer_single's. A problem
+ * whose scratch would exceed the array (about B * q_len * max_blocks_per_seq
+ * * 8 bytes of tagged scores, plus the split items' states) returns
+ * MSA_ERR_UNSUPPORTED before anything is enqueued. Every call on a GPU
+ * shares that GPU's array: calls that may overlap on one GPU (different
+ * streams, threads) race and must be serialised by the caller. The array
+ * keeps the last call's words; nothing in it needs clearing, because every
+ * word carries the epoch of the call that wrote it (and the array starts
+ * zeroed). The give-up count of msa_decode_layer_gave_up is not available
+ * for this entry; a give-up still shows as NaN rows and -1 selections. */
+msa_status_t msa_decode_layer_single_static(const msa_params_t* p, const msa_cache_t* cache,
+                                            const void* q, const void* idx_q, const float* idx_w,
+                                            void* out, float* lse, int32_t* sel_out, void* stream);
+
 /* msa_decode_layer_single with a tracing hook: when `events` is not NULL it
  * holds 2 hipEvent_t handles (NULL entries allowed) into which the kernel's
  * dispatch records its start and end (hipExtLaunchKernel). */

@@ -211,3 +211,22 @@ def test_debug_spin_limit_argument():
     L = msa.load()
     assert L.msa_debug_layer_spin_limit(-5) == _lib.MSA_ERR_INVALID_ARG
     assert L.msa_debug_layer_spin_limit(0) == _lib.MSA_OK
+
+
+def test_static_layer_rejects_oversized_scratch():
+    # the allocation-free entry refuses, before anything is enqueued, a
+    # problem whose tagged scores alone exceed its static scratch
+    fake = ctypes.c_void_p(256)
+    c = msa.Cache(k_data=fake, k_scale=fake, v_data=fake, v_scale=fake, k_tensor_scale=1.0, v_tensor_scale=1.0,
+                  idx_k=fake, idx_k_scale=fake, block_table=fake, ctx_lens=fake, idx_k_tensor_scale=1.0)
+    limit = _lib.load().msa_decode_layer_single_static
+    p = _params(num_seqs=1024, q_len=4, num_q_heads=64, num_kv_heads=4, idx_heads=8, max_blocks_per_seq=1024,
+                num_pages=4096, kv_dtype=1, idx_dtype=1)
+    st, err = _status(limit, ctypes.byref(p), ctypes.byref(c), fake, fake, fake, fake, None, None, None)
+    assert st == msa.MSA_ERR_UNSUPPORTED and "static scratch" in err, err
+    p = _params(kv_dtype=0)                     # bf16 K/V: not a single-launch problem
+    st, err = _status(limit, ctypes.byref(p), ctypes.byref(c), fake, fake, fake, fake, None, None, None)
+    assert st == msa.MSA_ERR_UNSUPPORTED
+    st, err = _status(limit, ctypes.byref(_params(kv_dtype=1, idx_dtype=1)), ctypes.byref(c), None, fake, fake, fake,
+                      None, None, None)
+    assert st == msa.MSA_ERR_INVALID_ARG

@@ -56,7 +56,7 @@ KERNELS = {
                          sources=("indexer.hip", "indexer_impl.hpp", "fmt.hpp", "indexer_args.hpp")),
     "decode_layer_single": dict(symbol="decode_layer_single_kernel",
                                 sources=("layer.hip", "indexer_impl.hpp", "attn_impl.hpp", "topk.hpp", "fmt.hpp",
-                                         "indexer_args.hpp", "msa_internal.hpp")),
+                                         "indexer_args.hpp", "msa_internal.hpp", "msa_api.hip")),
 }
 
 

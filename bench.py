@@ -10,13 +10,14 @@ indexer keys, q_len <= 4), else of msa_decode_layer (kernel 1: indexer +
 pool; kernel 2: selection + attention). Consecutive
 steps rotate over R device replicas of the inputs so that no step finds its
 bytes in the 256 MB Infinity Cache. Order: the device's attainable read and
-copy bandwidth (about 30 ms of streaming), W untimed steps, K steps whose
-kernels' dispatches record their own start and end events
-(hipExtLaunchKernel: the per-kernel durations of the two-kernel path), then
-the timed region: K steps between two HIP events on the launch stream. The
-GPU's clocks settle only after some milliseconds of load (a 50-step run
-right after start ran about 5% slower than later ones), so the measurements
-before the timed region also serve to bring it to its steady state.
+copy bandwidth (about 10 ms of streaming), W untimed steps, max(K, 500)
+steps whose kernels' dispatches record their own start and end events
+(hipExtLaunchKernel: the per-kernel durations), then the timed region: K
+steps between two HIP events on the launch stream, with a device
+synchronisation on both sides. The step time reaches its steady state only
+after some 50 ms of sustained load (passes in the first ~50 ms ran up to 20%
+slower), so the measurements before the timed region also bring the GPU to
+that state.
 Prints one JSON line on stdout (details on stderr):
 
   value        decode tokens/s per layer = B * T_q / step time
@@ -45,6 +46,11 @@ import time
 import numpy as np
 
 HBM_PEAK_GBPS = 8000.0
+# steps of the event-traced pass at least (before the timed region): on the
+# MI355X the step time reaches its steady state only after some 50 ms of
+# sustained load (20-step passes in the first ~50 ms ran 77-92 us, later ones
+# 75.5-77.8 us on the 128K workload)
+TRACED_MIN_STEPS = 500
 METRIC = "MSA decode tokens/s per layer at 128K ctx; achieved HBM GB/s vs 8 TB/s peak"
 ROOT = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(ROOT, "block_sparse_attention_kv_amd", "csrc")
@@ -511,7 +517,7 @@ def main():
     # ---- per-kernel durations: K steps whose kernels' dispatches record
     # their own start and end (these events lengthen the step a little, so
     # the step time comes from the plain pass below)
-    stage_all = run.traced(args.steps)
+    stage_all = run.traced(max(args.steps, TRACED_MIN_STEPS))
     stage_ms = [float(np.mean(d)) for d in stage_all]
     stage_pct = {n: [float(x) for x in np.percentile(d, [10, 50, 90])] for n, d in zip(run.stage_names, stage_all)}
     log("kernels (ms, event-traced pass): " + ", ".join("%s %.4f" % (n, v) for n, v in zip(run.stage_names, stage_ms)))

@@ -505,12 +505,16 @@ __global__ __launch_bounds__(kLayerThreads, kLayerWgsPerCu) void decode_layer_si
     return;
   }
   const int r = (int)blockIdx.x - L.idx_wgs;
-  // Selection, and an attention item until it knows its blocks, run at the
-  // highest wave priority: reading tagged words and selecting are a chain of
-  // dependent steps with little issue work, on the critical path of every
-  // item, while the waves they share a compute unit with stream keys.
-  __builtin_amdgcn_s_setprio(3);
   if (L.nsub == 0) {
+    // In the fused shape an item runs at the highest wave priority until it
+    // knows its blocks: reading the tagged scores and selecting are a chain
+    // of dependent steps with little issue work, on the critical path of
+    // every item, while the waves it shares a compute unit with stream keys.
+    // (In the split shape the selectors and attention workgroups fit beside
+    // the indexer workgroups and wait through the whole scan; at the top
+    // priority their polls slowed the scan: 46.4 against 45.2 us per step
+    // on the 512K workload.)
+    __builtin_amdgcn_s_setprio(3);
     if constexpr (MAXB == kTopkMax / kLayerWaves) fused_item(L, r, lds);
     return;
   }

@@ -365,13 +365,19 @@ __device__ __forceinline__ void stream_blocks(const AttnArgs& a, int g, int p, c
 }
 
 // acc := log-sum-exp merge of acc and the state (m2, l2, o2), in that order.
-__device__ __forceinline__ void merge_state(SoftmaxState& acc, float m2, float l2, const f32x4 (&o2)[8]) {
-  const float M = fmaxf(acc.m, m2);
-  const float a1 = lse_weight(acc.m, M), a2 = lse_weight(m2, M);
+// merge_state on ND of the 8 dim tiles (the max and sum as for all of them)
+template <int ND>
+__device__ __forceinline__ void merge_tiles(float& m, float& l, f32x4 (&o)[ND], float m2, float l2,
+                                            const f32x4 (&o2)[ND]) {
+  const float M = fmaxf(m, m2);
+  const float a1 = lse_weight(m, M), a2 = lse_weight(m2, M);
 #pragma unroll
-  for (int d = 0; d < 8; d++) acc.o[d] = acc.o[d] * a1 + o2[d] * a2;
-  acc.l = acc.l * a1 + l2 * a2;
-  acc.m = M;
+  for (int d = 0; d < ND; d++) o[d] = o[d] * a1 + o2[d] * a2;
+  l = l * a1 + l2 * a2;
+  m = M;
+}
+__device__ __forceinline__ void merge_state(SoftmaxState& acc, float m2, float l2, const f32x4 (&o2)[8]) {
+  merge_tiles<8>(acc.m, acc.l, acc.o, m2, l2, o2);
 }
 
 // Fixed-order tree merge of the W wave states through LDS slots (at least
@@ -406,22 +412,28 @@ __device__ __forceinline__ void merge_waves(SoftmaxState& st, uint8_t* lds, int 
 
 // bf16 output rows (and lse) of KV head g of row bt from wave 0's state
 // (called by wave 0 only).
-__device__ __forceinline__ void write_out(const AttnArgs& a, int bt, int g, const SoftmaxState& st, int lane) {
+// write_out of dim tiles d0 .. d0 + ND - 1 (held in o[0 .. ND)) of a state
+// with max m and sum l; the lse too when with_lse
+template <int ND>
+__device__ __forceinline__ void write_tiles(const AttnArgs& a, int bt, int g, float m, float l,
+                                            const f32x4 (&o)[ND], int d0, bool with_lse, int lane) {
   const int h = lane & 15, q4 = lane >> 4;
   if (h >= a.grp) return;
   const size_t row = (size_t)bt * a.Hq + g * a.grp + h;
-  const bool empty = !(st.l > 0.0f);
-  const float inv = empty ? 0.0f : a.v_scale_mul / st.l;
+  const bool empty = !(l > 0.0f);
+  const float inv = empty ? 0.0f : a.v_scale_mul / l;
   uint16_t* orow = a.out + row * kHeadDim;
 #pragma unroll
-  for (int d = 0; d < 8; d++) {
-    const f32x4 o = st.o[d];
+  for (int d = 0; d < ND; d++) {
     uint2 pk;
-    pk.x = f32x2_to_bf16x2(o[0] * inv, o[1] * inv);
-    pk.y = f32x2_to_bf16x2(o[2] * inv, o[3] * inv);
-    *reinterpret_cast<uint2*>(orow + 16 * d + 4 * q4) = pk;
+    pk.x = f32x2_to_bf16x2(o[d][0] * inv, o[d][1] * inv);
+    pk.y = f32x2_to_bf16x2(o[d][2] * inv, o[d][3] * inv);
+    *reinterpret_cast<uint2*>(orow + 16 * (d0 + d) + 4 * q4) = pk;
   }
-  if (a.lse && q4 == 0) a.lse[row] = empty ? -INFINITY : (st.m + __log2f(st.l)) * 0.69314718055994530942f;
+  if (with_lse && a.lse && q4 == 0) a.lse[row] = empty ? -INFINITY : (m + __log2f(l)) * 0.69314718055994530942f;
+}
+__device__ __forceinline__ void write_out(const AttnArgs& a, int bt, int g, const SoftmaxState& st, int lane) {
+  write_tiles<8>(a, bt, g, st.m, st.l, st.o, 0, true, lane);
 }
 
 // NaN output rows and lse of KV head g of row bt: the item's inputs never

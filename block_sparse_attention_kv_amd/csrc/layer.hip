@@ -76,6 +76,8 @@ constexpr int kSpinLimit = 1 << 20;  // polls of one chunk of tagged words (a me
 constexpr int kSubBlocks = 1024;     // blocks per selector: one 256-block chunk per wave
 constexpr int kCandWords = 1 + 3 * kTopkMax;  // words of a candidate record in use
 
+typedef uint64_t u64x2 __attribute__((ext_vector_type(2)));
+
 // Poll limit of the next launches (0: kSpinLimit); set by a debug export.
 std::atomic<int> g_spin_limit{0};
 
@@ -273,10 +275,14 @@ __device__ void select_range(const LayerArgs& L, int tok, int j, uint8_t* lds) {
   if (stale && lane == 0) report_give_up(L);
 }
 
-// Tagged partial softmax state of one split: per head h, 128 O words, m, l
-// (a row of kPartRow words); lane (h, q4) holds O dims 16d + 4*q4 + r.
-__device__ __forceinline__ uint64_t* partial_row(const LayerArgs& L, int item, int split, int h) {
-  return L.ws.partials + (((size_t)item * (L.aa.splits - 1) + split) * 16 + h) * kPartRow;
+// Tagged partial softmax state of one split (kStateWords words): word
+// 64 (4d + r) + lane holds O element (d, r) of the publishing wave's lane
+// (h, q4) = (lane & 15, lane >> 4), i.e. head h, dim 16d + 4 q4 + r; words
+// 2048 + h and 2112 + h hold m and l of head h. A reading lane loads the
+// words of the same lane index, so every load and store instruction covers
+// 512 contiguous bytes.
+__device__ __forceinline__ uint64_t* split_state(const LayerArgs& L, int item, int split) {
+  return L.ws.partials + ((size_t)item * (L.aa.splits - 1) + split) * kStateWords;
 }
 
 // Attention of KV head g of query token tok, split `split` of S.
@@ -343,7 +349,8 @@ __device__ void split_item(const LayerArgs& L, int tok, int g, int split, uint8_
     }
     stale = __ballot(stale) != 0ull || !got;
     wave_lds_sync();
-    // keys of the valid candidates: (ranking key << 32) | (8191 - block) << 7 | slot
+    // keys of the valid candidates: (ranking key << 32) | 1 << 20 |
+    // (8191 - block) << 7 | slot; bit 20 keeps every valid key nonzero
     uint64_t k[2];
     int total = 0;
 #pragma unroll
@@ -355,27 +362,51 @@ __device__ void split_item(const LayerArgs& L, int tok, int g, int split, uint8_
         const int blk = cblk[c];
         valid = blk >= 0 && blk < a.maxb && blk * kBlock <= p;
       }
-      k[s2] = valid ? (cand[c] << 32) | ((uint64_t)(8191 - cblk[c]) << 7) | (uint64_t)c : 0ull;
+      k[s2] = valid ? (cand[c] << 32) | (1ull << 20) | ((uint64_t)(8191 - cblk[c]) << 7) | (uint64_t)c : 0ull;
       total += __popcll(__ballot(valid));
     }
     const int K = min(a.top_k, total);
     int cnt = 0;
     if (K > 0) {
-      const uint64_t T = kth_threshold<2>(k, K);
-      __shared__ uint64_t fin[kTopkMax];
-      compact_ge<2>(k, T, fin);
+      // the rank of every key among all candidates (the number of larger
+      // keys; keys are unique): at most 128 keys, read from LDS two at a
+      // time by every lane at once, a fixed cost where a threshold search
+      // over 64-bit keys is a long chain of dependent counts
+      __shared__ __attribute__((aligned(16))) uint64_t ckey[kTopkMax * 8];
+      __shared__ int32_t wcand[kTopkMax];
+      ckey[lane] = k[0];
+      ckey[lane + 64] = k[1];
       wave_lds_sync();
-      // ascending block order: the rank of each winner among the winners;
-      // then the attended ones (page present) keep that order
+      const int ncand = nrec * kTopkMax;
+      int rk0 = 0, rk1 = 0;
+      if (ncand <= 64) {
+#pragma unroll 8
+        for (int j = 0; j < ncand; j += 2) {
+          const u64x2 two = *reinterpret_cast<const u64x2*>(ckey + j);
+          rk0 += (two[0] > k[0] ? 1 : 0) + (two[1] > k[0] ? 1 : 0);
+        }
+      } else {
+#pragma unroll 8
+        for (int j = 0; j < ncand; j += 2) {
+          const u64x2 two = *reinterpret_cast<const u64x2*>(ckey + j);
+          rk0 += (two[0] > k[0] ? 1 : 0) + (two[1] > k[0] ? 1 : 0);
+          rk1 += (two[0] > k[1] ? 1 : 0) + (two[1] > k[1] ? 1 : 0);
+        }
+      }
+      // the winners (rank < K), one LDS slot per rank
+      if (k[0] != 0ull && rk0 < K) wcand[rk0] = lane;
+      if (k[1] != 0ull && rk1 < K) wcand[rk1] = lane + 64;
+      wave_lds_sync();
+      // ascending block order: the rank of each winner's block among the
+      // winners'; then the attended ones (page present) keep that order
       __shared__ int32_t sblk[kTopkMax], spage[kTopkMax];
-      int rank = 0;
+      const int c = lane < K ? wcand[lane] : 0;
+      const int wblk = lane < K ? cblk[c] : INT_MAX;
+      const int rank = rank_among16(wblk);  // the candidates' blocks are distinct
       if (lane < K) {
-        const int c = (int)(fin[lane] & 127u);
-        const int blk = cblk[c];
-        for (int q = 0; q < K; q++) rank += (8191 - (int)((fin[q] >> 7) & 8191u)) < blk;
-        sblk[rank] = blk;
+        sblk[rank] = wblk;
         spage[rank] = cpage[c];
-        sel_all[rank] = blk;
+        sel_all[rank] = wblk;
       }
       wave_lds_sync();
       // lane r: the winner of rank r
@@ -416,52 +447,61 @@ __device__ void split_item(const LayerArgs& L, int tok, int g, int split, uint8_
   }
   if (split < S - 1) {  // publish this split's state
     if (wave != 0) return;
-    uint64_t* row = partial_row(L, item, split, h);
+    uint64_t* row = split_state(L, item, split);
 #pragma unroll
     for (int d = 0; d < 8; d++)
 #pragma unroll
-      for (int r = 0; r < 4; r++) store_word(row + 16 * d + 4 * q4 + r, tag | __float_as_uint(st.o[d][r]));
+      for (int r = 0; r < 4; r++) store_word(row + 64 * (4 * d + r) + lane, tag | __float_as_uint(st.o[d][r]));
     if (q4 == 0) {
-      store_word(row + 128, tag | __float_as_uint(st.m));
-      store_word(row + 129, tag | __float_as_uint(st.l));
+      store_word(row + 2048 + h, tag | __float_as_uint(st.m));
+      store_word(row + 2112 + h, tag | __float_as_uint(st.l));
     }
     return;
   }
   // last split: wave w (1 <= w < S) reads split w-1's state into LDS slot
-  // w-1; wave 0 then merges splits 0 .. S-2 and its own, in that order.
+  // w-1 and wave 0 puts its own in slot S-1; then wave w merges dim tiles
+  // 2w and 2w+1 of splits 0, 1, ..., S-1, in that order, and writes them.
   // Each reading wave first waits on one word of its split (head 0's l,
   // stored last), so that a state still being written costs one load per
   // poll, not a whole row.
   float* slots = reinterpret_cast<float*>(lds);
   __syncthreads();  // the wave-merge slots are free again
-  if (wave >= 1 && wave < S) {
-    const uint64_t* row = partial_row(L, item, wave - 1, h);
+  if (wave == 0) {
+    float* sl = slots + (S - 1) * kSlotFloats;
+#pragma unroll
+    for (int d = 0; d < 8; d++) *reinterpret_cast<f32x4*>(sl + h * kHeadDim + 16 * d + 4 * q4) = st.o[d];
+    if (q4 == 0) {
+      sl[16 * kHeadDim + h] = st.m;
+      sl[16 * kHeadDim + 16 + h] = st.l;
+    }
+  } else if (wave < S) {
+    const uint64_t* row = split_state(L, item, wave - 1);
     uint64_t wo[32], wm = 0, wl = 0;
     bool got = false;
-    {
-      const uint64_t* last = partial_row(L, item, wave - 1, 0) + 129;
-      for (int polls = 0; polls < a.spin_limit; polls++) {
-        if ((uint32_t)(__builtin_amdgcn_readfirstlane((int)(load_word(last) >> 32))) == a.epoch) break;
-        __builtin_amdgcn_s_sleep(1);
-      }
+    for (int polls = 0; polls < a.spin_limit; polls++) {  // head 0's l, stored last
+      if ((uint32_t)(__builtin_amdgcn_readfirstlane((int)(load_word(row + 2112) >> 32))) == a.epoch) break;
+      __builtin_amdgcn_s_sleep(1);
     }
+    // then every word, again only the ones still missing
+#pragma unroll
+    for (int j = 0; j < 32; j++) wo[j] = load_word(row + 64 * j + lane);
+    wm = load_word(row + 2048 + h);
+    wl = load_word(row + 2112 + h);
     for (int polls = 0; polls < a.spin_limit; polls++) {
-      if (polls) __builtin_amdgcn_s_sleep(1);
       bool miss = false;
 #pragma unroll
-      for (int d = 0; d < 8; d++)
-#pragma unroll
-        for (int r = 0; r < 4; r++) {
-          wo[4 * d + r] = load_word(row + 16 * d + 4 * q4 + r);
-          miss |= (uint32_t)(wo[4 * d + r] >> 32) != a.epoch;
-        }
-      wm = load_word(row + 128);
-      wl = load_word(row + 129);
+      for (int j = 0; j < 32; j++) miss |= (uint32_t)(wo[j] >> 32) != a.epoch;
       miss |= (uint32_t)(wm >> 32) != a.epoch || (uint32_t)(wl >> 32) != a.epoch;
       if (__ballot(miss) == 0ull) {
         got = true;
         break;
       }
+      __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+      for (int j = 0; j < 32; j++)
+        if ((uint32_t)(wo[j] >> 32) != a.epoch) wo[j] = load_word(row + 64 * j + lane);
+      if ((uint32_t)(wm >> 32) != a.epoch) wm = load_word(row + 2048 + h);
+      if ((uint32_t)(wl >> 32) != a.epoch) wl = load_word(row + 2112 + h);
     }
     float* sl = slots + (wave - 1) * kSlotFloats;
 #pragma unroll
@@ -475,25 +515,29 @@ __device__ void split_item(const LayerArgs& L, int tok, int g, int split, uint8_
     if (lane == 0) gave[wave] = got ? 0 : 1;
   }
   __syncthreads();
-  if (wave != 0) return;
   bool lost = false;
   for (int w = 1; w < S; w++) lost |= gave[w] != 0;
   if (lost) {
-    write_invalid(a, tok, g, lane, kWave);
-    if (lane == 0) report_give_up(L);
+    if (wave == 0) {
+      write_invalid(a, tok, g, lane, kWave);
+      if (lane == 0) report_give_up(L);
+    }
     return;
   }
-  SoftmaxState acc;
-  init_state(acc);
-  for (int s = 0; s < S - 1; s++) {
-    const float* sl = slots + s * kSlotFloats;
-    f32x4 o2[8];
+  constexpr int ND = 8 / kLayerWaves;
+  const int d0 = ND * wave;
+  float m = -INFINITY, l = 0.0f;
+  f32x4 o[ND];
 #pragma unroll
-    for (int d = 0; d < 8; d++) o2[d] = *reinterpret_cast<const f32x4*>(sl + h * kHeadDim + 16 * d + 4 * q4);
-    merge_state(acc, sl[16 * kHeadDim + h], sl[16 * kHeadDim + 16 + h], o2);
+  for (int i = 0; i < ND; i++) o[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int s = 0; s < S; s++) {
+    const float* sl = slots + s * kSlotFloats;
+    f32x4 o2[ND];
+#pragma unroll
+    for (int i = 0; i < ND; i++) o2[i] = *reinterpret_cast<const f32x4*>(sl + h * kHeadDim + 16 * (d0 + i) + 4 * q4);
+    merge_tiles<ND>(m, l, o, sl[16 * kHeadDim + h], sl[16 * kHeadDim + 16 + h], o2);
   }
-  merge_state(acc, st.m, st.l, st.o);
-  write_out(a, tok, g, acc, lane);
+  write_tiles<ND>(a, tok, g, m, l, o, d0, wave == 0, lane);
 }
 
 template <int KF, int HP, int TQ, int MAXB>
@@ -589,7 +633,7 @@ hipError_t launch_layer_single(const IndexerArgs& ia, const AttnArgs& aa, const 
   size_t lds = ((size_t)ia.B + 1) * sizeof(int32_t);
   const size_t pages = (size_t)aa.maxb * sizeof(int32_t);
   const size_t stage = (size_t)kLayerWaves * 1024 * 2;
-  const size_t merge = (size_t)(kLayerWaves - 1) * kSlotFloats * 4;
+  const size_t merge = (size_t)kLayerWaves * kSlotFloats * 4;  // the last split's S <= 4 states
   lds = lds > pages ? lds : pages;
   lds = lds > stage ? lds : stage;
   lds = lds > merge ? lds : merge;

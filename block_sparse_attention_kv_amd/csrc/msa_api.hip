@@ -136,7 +136,7 @@ Layout layout(const msa_params_t* p) {
   L.tagged_off = align256(bt * p->max_blocks_per_seq * sizeof(float));
   L.records_off = L.tagged_off + align256(bt * p->max_blocks_per_seq * sizeof(uint64_t));
   L.lpart_off = L.records_off + align256(bt * layer_selectors(p->max_blocks_per_seq) * kRecordWords * sizeof(uint64_t));
-  L.gave_up_off = L.lpart_off + align256(items * (kLayerMaxSplits - 1) * 16 * kPartRow * sizeof(uint64_t));
+  L.gave_up_off = L.lpart_off + align256(items * (kLayerMaxSplits - 1) * kStateWords * sizeof(uint64_t));
   L.part_off = L.gave_up_off + 256;
   const size_t part = L.splits > 1 ? items * L.splits * 16 * kPartRow * sizeof(float) : 0;
   L.arrive_off = L.part_off + align256(part);
@@ -219,22 +219,20 @@ bool recalled_epoch(const void* ws, uint32_t* e) {
 }
 
 // Shape of the single launch. With at least one (sequence, token, KV head)
-// item per compute unit, or contexts of at most 1,024 blocks, one workgroup
-// per item selects and attends (fused). With fewer items over longer
-// contexts, a selection by one workgroup (four waves over thousands of
-// blocks) and a lone item per compute unit streaming four blocks per wave
-// leave the chip idle: per token, selectors over 1,024-block ranges, and
-// each item split over 4 workgroups of one block per wave. A debug export
-// can force the shape: 1 = fused, 2 or 4 = split with that many workgroups
-// per item.
-constexpr int kSplitMinBlocks = 1024;
+// item per compute unit, one workgroup per item selects and attends (fused).
+// With fewer items a lone item per compute unit streaming four blocks per
+// wave (and, over thousands of blocks, a selection by one workgroup) leaves
+// the chip idle: per token, selectors over 1,024-block ranges, and each item
+// split over 4 workgroups of one block per wave (32K-token contexts, 16
+// items: 22.6 against 23.9 us per step fused). A debug export can force the
+// shape: 1 = fused, 2 or 4 = split with that many workgroups per item.
 std::atomic<int> g_layer_splits{0};
 int device_cus();
 int layer_splits(const msa_params_t* p) {
   const int forced = g_layer_splits.load(std::memory_order_relaxed);
   if (forced > 0) return forced;
   const int64_t items = (int64_t)p->num_seqs * p->q_len * p->num_kv_heads;
-  return (items >= (int64_t)device_cus() || p->max_blocks_per_seq <= kSplitMinBlocks) ? 1 : 4;
+  return items >= (int64_t)device_cus() ? 1 : 4;
 }
 
 // Compute units of the current device (the persistent indexer grid is sized
@@ -394,7 +392,7 @@ StaticLayout static_layout(const msa_params_t* p, int splits) {
   L.tagged_off = 0;
   L.records_off = align256(bt * p->max_blocks_per_seq * sizeof(uint64_t));
   L.lpart_off = L.records_off + align256(bt * layer_selectors(p->max_blocks_per_seq) * kRecordWords * sizeof(uint64_t));
-  L.gave_up_off = L.lpart_off + (splits > 1 ? align256(items * (splits - 1) * 16 * kPartRow * sizeof(uint64_t)) : 0);
+  L.gave_up_off = L.lpart_off + (splits > 1 ? align256(items * (splits - 1) * kStateWords * sizeof(uint64_t)) : 0);
   L.total = L.gave_up_off + 256;
   return L;
 }

@@ -114,10 +114,14 @@ constexpr int kLayerMaxIdxWgs = 4096;
 // (ranking key, logical block, page); every word tagged with the call's
 // epoch. Padded to kRecordWords words.
 constexpr int kRecordWords = 56;
+// Tagged softmax state of one split of a split item: 34 rows of 64 words, row
+// j < 32 holding O element j of every lane of the publishing wave, rows 32
+// and 33 m and l of the 16 heads.
+constexpr int kStateWords = 34 * 64;
 constexpr uint32_t kRecordStale = 0x80000000u;
 struct LayerScratch {
   uint64_t* records;            // [B * Tq][selectors][kRecordWords] (split shape)
-  uint64_t* partials;           // [items][splits - 1][16][kPartRow] tagged softmax states (splits > 1)
+  uint64_t* partials;           // [items][splits - 1][kStateWords] tagged softmax states (splits > 1)
   unsigned long long* gave_up;  // (epoch << 32) | workgroups of that call that gave up a wait
 };
 // Selectors per query token in the split shape for a block table of

@@ -19,6 +19,8 @@
 // one wave then reduces the winners of all waves the same way and sorts the
 // final k by block index. The result does not depend on thread timing.
 #pragma once
+#include <climits>
+
 #include "fmt.hpp"
 
 namespace msa {
@@ -79,8 +81,9 @@ __device__ __forceinline__ uint32_t wave_extremum_u32(uint32_t v) {
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) { return wave_extremum_u32<true>(v); }
 __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) { return wave_extremum_u32<false>(v); }
 
-// Threshold T with exactly K keys >= T, K <= number of nonzero keys (keys
-// are unique). Returns T (uniform).
+// Threshold T with exactly K keys >= T, where K <= have, the number of
+// nonzero keys (keys are unique). Returns T (uniform). With K = have every
+// nonzero key is a winner and T = 1 without a search.
 //
 // The search starts below the bits that all nonzero, non-forced keys share
 // (the common prefix of their largest and smallest high words): a candidate
@@ -88,7 +91,8 @@ __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) { return wave_extre
 // the one forced key above it, fewer than K >= 2. With K = 1, or with no
 // such key, the search covers all 64 bits.
 template <int NK>
-__device__ __forceinline__ uint64_t kth_threshold(const uint64_t (&k)[NK], int K) {
+__device__ __forceinline__ uint64_t kth_threshold(const uint64_t (&k)[NK], int K, int have) {
+  if (K >= have) return 1ull;
   uint32_t hmax = 0u, hmin = 0xFFFFFFFFu;
 #pragma unroll
   for (int j = 0; j < NK; j++) {
@@ -121,6 +125,16 @@ __device__ __forceinline__ uint64_t kth_threshold(const uint64_t (&k)[NK], int K
     }
   }
   return T;
+}
+
+// Number of lanes among 0..15 whose v is below this lane's v, read from the
+// lanes' registers (no LDS round trips). All 64 lanes call it; a lane
+// outside the ranked set passes INT_MAX, which no value counts.
+__device__ __forceinline__ int rank_among16(int v) {
+  int r = 0;
+#pragma unroll
+  for (int q = 0; q < kTopkCap; q++) r += __builtin_amdgcn_readlane(v, q) < v ? 1 : 0;
+  return r;
 }
 
 // Writes the keys >= T of the NK slots (exactly `cnt` of them) to dst[0..cnt)
@@ -233,9 +247,9 @@ __device__ int block_topk(ScoreFn score, PageFn page, int32_t* pages, int n, int
     const int K = min(top_k, have);
     if (base == lo) {  // first chunk: no winners carried yet
       const uint64_t (&k4)[4] = reinterpret_cast<const uint64_t (&)[4]>(k);
-      compact_ge<4>(k4, kth_threshold<4>(k4, K), s.win[wave]);
+      compact_ge<4>(k4, kth_threshold<4>(k4, K, have), s.win[wave]);
     } else {
-      compact_ge<5>(k, kth_threshold<5>(k, K), s.win[wave]);
+      compact_ge<5>(k, kth_threshold<5>(k, K, have), s.win[wave]);
     }
     wave_lds_sync();
     nc = K;
@@ -267,15 +281,12 @@ __device__ int block_topk(ScoreFn score, PageFn page, int32_t* pages, int n, int
 #pragma unroll
     for (int w = 0; w < NW; w++) have += s.nwin[w];
     const int K = min(top_k, have);
-    const uint64_t T = kth_threshold<NJ>(k, K);
+    const uint64_t T = kth_threshold<NJ>(k, K, have);
     compact_ge<NJ>(k, T, s.fin);
     wave_lds_sync();
-    if (lane < K) {
-      const int mine = (int)(0xFFFFFFFFu - (uint32_t)s.fin[lane]);
-      int rank = 0;
-      for (int q = 0; q < K; q++) rank += (int)(0xFFFFFFFFu - (uint32_t)s.fin[q]) < mine;
-      out[rank] = mine;
-    }
+    const int mine = lane < K ? (int)(0xFFFFFFFFu - (uint32_t)s.fin[lane]) : INT_MAX;
+    const int rank = rank_among16(mine);
+    if (lane < K) out[rank] = mine;
     if (lane == 0) s.nwin[0] = K;
   }
   __syncthreads();

@@ -289,10 +289,7 @@ __device__ __forceinline__ uint64_t* split_state(const LayerArgs& L, int item, i
 template <int MAXB>
 __device__ void split_item(const LayerArgs& L, int tok, int g, int split, uint8_t* lds) {
   const AttnArgs& a = L.aa;
-  __shared__ uint64_t cand[kTopkMax * 8];   // winners of the final merge (keys), then their order
-  __shared__ int32_t cblk[kTopkMax * 8], cpage[kTopkMax * 8];
   __shared__ int32_t blist[kTopkMax], plist[kTopkMax], sel_all[kTopkMax];
-  __shared__ int32_t ccount[8];             // candidates per record
   __shared__ int32_t nlist, bad, gave[kLayerWaves];
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -307,62 +304,64 @@ __device__ void split_item(const LayerArgs& L, int tok, int g, int split, uint8_
 
   // ---- the token's candidate records -> the top-k blocks -> this split's share
   if (wave == 0) {
+    // candidate c = 16 r + e (record r, entry e) belongs to lane c % 64,
+    // slot c / 64 (a second slot only with more than 4 records); the lane
+    // reads the record's header and the entry's key, block and page words
     const int nrec = L.nsub;
-    const int nw = nrec * kRecordWords;  // words to read (whole padded records)
-    const uint64_t* src = cand_record(L, tok, 0);
-    // up to 8 records of 56 words: 7 words per lane
-    uint64_t w[7];
-    bool got = true, stale = false;
+    const int nslot = nrec > 4 ? 2 : 1;
+    uint64_t w[2][4];
+    bool got = true;
+#pragma unroll
+    for (int sl = 0; sl < 2; sl++) {
+      const int c = lane + 64 * sl, r = c >> 4, e = c & 15;
+      const bool use = sl < nslot && r < nrec;
+      const uint64_t* rec = cand_record(L, tok, use ? r : 0);
+#pragma unroll
+      for (int f = 0; f < 4; f++) w[sl][f] = use ? load_word(rec + (f == 0 ? 0 : 3 * e + f)) : tag;
+    }
     for (int polls = 0;; polls++) {
       bool miss = false;
 #pragma unroll
-      for (int i = 0; i < 7; i++) {
-        const int x = lane + 64 * i;
-        const bool used = x < nw && x % kRecordWords < kCandWords;
-        if (polls == 0 || (used && (uint32_t)(w[i] >> 32) != a.epoch)) w[i] = used ? load_word(src + x) : tag;
-        miss |= (uint32_t)(w[i] >> 32) != a.epoch;
-      }
+      for (int sl = 0; sl < 2; sl++)
+#pragma unroll
+        for (int f = 0; f < 4; f++) miss |= (uint32_t)(w[sl][f] >> 32) != a.epoch;
       if (__ballot(miss) == 0ull) break;
       if (polls + 1 >= a.spin_limit) {
         got = false;
         break;
       }
       __builtin_amdgcn_s_sleep(1);
-    }
-    // candidates: record r entry e at words 1 + 3e (key), 2 + 3e (block), 3 + 3e (page)
 #pragma unroll
-    for (int i = 0; i < 7; i++) {
-      const int x = lane + 64 * i;
-      if (x < nw) {
-        const int r = x / kRecordWords, o = x % kRecordWords;
-        if (o == 0) {
-          stale |= ((uint32_t)w[i] & kRecordStale) != 0u || ((uint32_t)w[i] & 0xFFFFu) > kTopkMax;
-          ccount[r] = (int)((uint32_t)w[i] & 0xFFFFu);
-        }
-        if (o >= 1 && o < kCandWords) {
-          const int e = (o - 1) / 3, f = (o - 1) % 3, c = r * kTopkMax + e;
-          if (f == 0) cand[c] = (uint32_t)w[i];
-          else if (f == 1) cblk[c] = (int)(uint32_t)w[i];
-          else cpage[c] = (int)(uint32_t)w[i];
-        }
+      for (int sl = 0; sl < 2; sl++) {
+        const int c = lane + 64 * sl, r = c >> 4, e = c & 15;
+        const uint64_t* rec = cand_record(L, tok, r < nrec ? r : 0);
+#pragma unroll
+        for (int f = 0; f < 4; f++)
+          if ((uint32_t)(w[sl][f] >> 32) != a.epoch) w[sl][f] = load_word(rec + (f == 0 ? 0 : 3 * e + f));
       }
     }
-    stale = __ballot(stale) != 0ull || !got;
-    wave_lds_sync();
+    // a record marked stale (its selector gave up) or malformed spoils the selection
+    bool spoilt = false;
+#pragma unroll
+    for (int sl = 0; sl < 2; sl++) {
+      const uint32_t hdr = (uint32_t)w[sl][0];
+      spoilt |= (hdr & kRecordStale) != 0u || (hdr & 0xFFFFu) > (uint32_t)kTopkMax;
+    }
+    const bool stale = __ballot(spoilt) != 0ull || !got;
     // keys of the valid candidates: (ranking key << 32) | 1 << 20 |
-    // (8191 - block) << 7 | slot; bit 20 keeps every valid key nonzero
+    // (8191 - block) << 7 | c; bit 20 keeps every valid key nonzero
     uint64_t k[2];
-    int total = 0;
+    int blk[2], page[2], total = 0;
 #pragma unroll
-    for (int s2 = 0; s2 < 2; s2++) {
-      const int c = lane + 64 * s2;
-      const int r = c / kTopkMax, e = c % kTopkMax;
-      bool valid = false;
-      if (r < nrec && !stale && e < ccount[r]) {
-        const int blk = cblk[c];
-        valid = blk >= 0 && blk < a.maxb && blk * kBlock <= p;
-      }
-      k[s2] = valid ? (cand[c] << 32) | (1ull << 20) | ((uint64_t)(8191 - cblk[c]) << 7) | (uint64_t)c : 0ull;
+    for (int sl = 0; sl < 2; sl++) {
+      const int c = lane + 64 * sl, r = c >> 4, e = c & 15;
+      blk[sl] = (int)(uint32_t)w[sl][2];
+      page[sl] = (int)(uint32_t)w[sl][3];
+      const bool valid = !stale && sl < nslot && r < nrec && e < (int)((uint32_t)w[sl][0] & 0xFFFFu) &&
+                         blk[sl] >= 0 && blk[sl] < a.maxb && blk[sl] * kBlock <= p;
+      k[sl] = valid ? ((uint64_t)(uint32_t)w[sl][1] << 32) | (1ull << 20) | ((uint64_t)(8191 - blk[sl]) << 7) |
+                          (uint64_t)c
+                    : 0ull;
       total += __popcll(__ballot(valid));
     }
     const int K = min(a.top_k, total);
@@ -373,13 +372,13 @@ __device__ void split_item(const LayerArgs& L, int tok, int g, int split, uint8_
       // time by every lane at once, a fixed cost where a threshold search
       // over 64-bit keys is a long chain of dependent counts
       __shared__ __attribute__((aligned(16))) uint64_t ckey[kTopkMax * 8];
-      __shared__ int32_t wcand[kTopkMax];
+      __shared__ int32_t wblk_lds[kTopkMax], wpage_lds[kTopkMax];
       ckey[lane] = k[0];
-      ckey[lane + 64] = k[1];
+      if (nslot > 1) ckey[lane + 64] = k[1];
       wave_lds_sync();
       const int ncand = nrec * kTopkMax;
       int rk0 = 0, rk1 = 0;
-      if (ncand <= 64) {
+      if (nslot == 1) {
 #pragma unroll 8
         for (int j = 0; j < ncand; j += 2) {
           const u64x2 two = *reinterpret_cast<const u64x2*>(ckey + j);
@@ -393,32 +392,30 @@ __device__ void split_item(const LayerArgs& L, int tok, int g, int split, uint8_
           rk1 += (two[0] > k[1] ? 1 : 0) + (two[1] > k[1] ? 1 : 0);
         }
       }
-      // the winners (rank < K), one LDS slot per rank
-      if (k[0] != 0ull && rk0 < K) wcand[rk0] = lane;
-      if (k[1] != 0ull && rk1 < K) wcand[rk1] = lane + 64;
-      wave_lds_sync();
-      // ascending block order: the rank of each winner's block among the
-      // winners'; then the attended ones (page present) keep that order
-      __shared__ int32_t sblk[kTopkMax], spage[kTopkMax];
-      const int c = lane < K ? wcand[lane] : 0;
-      const int wblk = lane < K ? cblk[c] : INT_MAX;
-      const int rank = rank_among16(wblk);  // the candidates' blocks are distinct
-      if (lane < K) {
-        sblk[rank] = wblk;
-        spage[rank] = cpage[c];
-        sel_all[rank] = wblk;
+      // the winners (rank < K) to lanes 0 .. K-1, in rank order
+      if (k[0] != 0ull && rk0 < K) {
+        wblk_lds[rk0] = blk[0];
+        wpage_lds[rk0] = page[0];
+      }
+      if (k[1] != 0ull && rk1 < K) {
+        wblk_lds[rk1] = blk[1];
+        wpage_lds[rk1] = page[1];
       }
       wave_lds_sync();
-      // lane r: the winner of rank r
-      const int blk = lane < K ? sblk[lane] : -1, page = lane < K ? spage[lane] : -1;
-      const bool ok = lane < K && page >= 0 && page < a.num_pages;
-      const uint64_t bal = __ballot(ok);
-      const int apos = __popcll(bal & ((1ull << lane) - 1ull));
-      cnt = __popcll(bal);
+      const int wblk = lane < K ? wblk_lds[lane] : INT_MAX;
+      const int wpage = lane < K ? wpage_lds[lane] : -1;
+      const bool ok = lane < K && wpage >= 0 && wpage < a.num_pages;
+      // ascending block order (the candidates' blocks are distinct): the
+      // winner's position among all winners and among the attended ones
+      // (page present)
+      const int brank = rank_among16(wblk);
+      const int apos = rank_among16(ok ? wblk : INT_MAX);
+      if (lane < K) sel_all[brank] = wblk;
+      cnt = __popcll(__ballot(ok));
       const int per = (cnt + S - 1) / S, first = split * per;
       if (ok && apos >= first && apos < first + per) {
-        blist[apos - first] = blk;
-        plist[apos - first] = page;
+        blist[apos - first] = wblk;
+        plist[apos - first] = wpage;
       }
       if (lane == 0) nlist = max(0, min(per, cnt - first));
     } else if (lane == 0) {

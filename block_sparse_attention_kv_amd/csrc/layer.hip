@@ -133,18 +133,41 @@ __device__ __forceinline__ void attend_list(const AttnArgs& a, int tok, int g, i
 }
 
 // Leaves the top wave priority once the blocks are known: the later half of
-// the items, dispatched last, ends the kernel, and its waves share compute
-// units with older attention waves that win issue arbitration by age.
-__device__ __forceinline__ void drop_priority(const AttnArgs& a, int item) {
-  if (2 * item >= a.B * a.Tq * a.Hkv) __builtin_amdgcn_s_setprio(1);
+// the items (by dispatch position `pos` among the items), dispatched last,
+// ends the kernel, and its waves share compute units with older attention
+// waves that win issue arbitration by age.
+__device__ __forceinline__ void drop_priority(const AttnArgs& a, int pos) {
+  if (2 * pos >= a.B * a.Tq * a.Hkv) __builtin_amdgcn_s_setprio(1);
   else __builtin_amdgcn_s_setprio(0);
+}
+
+// Fused shape: the item (token * Hkv + g) at dispatch position r. The q_len
+// items of one (sequence, KV head) sit 8 positions apart, so that they run
+// on one XCD (workgroups go to the 8 XCDs in turn) and the blocks several of
+// their tokens select -- the query positions' own block always -- can come
+// from that XCD's L2 (128K spec-verify: 439.7 against 443.3 MB fetched per
+// step). Groups of 8 (sequence, KV head) pairs take 8 * q_len positions;
+// the pairs past the last full group keep their tokens adjacent.
+__device__ __forceinline__ int fused_item_at(const AttnArgs& a, int r) {
+  const int Tq = a.Tq, Hkv = a.Hkv, full = (a.B * Hkv / 8) * 8;
+  int pair, t;
+  if (r < full * Tq) {
+    const int grp = r / (8 * Tq), rem = r - grp * 8 * Tq;
+    t = rem / 8;
+    pair = 8 * grp + rem % 8;
+  } else {
+    const int r2 = r - full * Tq;
+    pair = full + r2 / Tq;
+    t = r2 % Tq;
+  }
+  return ((pair / Hkv) * Tq + t) * Hkv + pair % Hkv;
 }
 
 // ---------------------------------------------------------------- fused shape
 
-// Item `item` = (token, KV head): selection from the token's tagged pooled
-// scores, then attention over all selected blocks.
-__device__ void fused_item(const LayerArgs& L, int item, uint8_t* lds) {
+// Item `item` = (token, KV head), at dispatch position `pos`: selection from
+// the token's tagged pooled scores, then attention over all selected blocks.
+__device__ void fused_item(const LayerArgs& L, int item, int pos, uint8_t* lds) {
   const AttnArgs& a = L.aa;
   __shared__ TopkLds tk;
   __shared__ int32_t sel_lds[kTopkMax], blist[kTopkMax], plist[kTopkMax];
@@ -192,7 +215,7 @@ __device__ void fused_item(const LayerArgs& L, int item, uint8_t* lds) {
     if (lane == 0) nlist = __popcll(bal);
   }
   __syncthreads();
-  drop_priority(a, item);
+  drop_priority(a, pos);
   SoftmaxState st;
   attend_list<kTopkMax / kLayerWaves>(a, tok, g, p, qraw, blist, plist, __builtin_amdgcn_readfirstlane(nlist), lds,
                                       wave, lane, st);
@@ -563,7 +586,7 @@ __global__ __launch_bounds__(kLayerThreads, kLayerWgsPerCu) void decode_layer_si
     // priority their polls slowed the scan: 46.4 against 45.2 us per step
     // on the 512K workload.)
     __builtin_amdgcn_s_setprio(3);
-    if constexpr (MAXB == kTopkMax / kLayerWaves) fused_item(L, r, lds);
+    if constexpr (MAXB == kTopkMax / kLayerWaves) fused_item(L, fused_item_at(L.aa, r), r, lds);
     return;
   }
   const int per_tok = L.nsub + L.aa.Hkv * L.aa.splits;

@@ -141,26 +141,19 @@ __device__ __forceinline__ void drop_priority(const AttnArgs& a, int pos) {
   else __builtin_amdgcn_s_setprio(0);
 }
 
-// Fused shape: the item (token * Hkv + g) at dispatch position r. The q_len
-// items of one (sequence, KV head) sit 8 positions apart, so that they run
-// on one XCD (workgroups go to the 8 XCDs in turn) and the blocks several of
-// their tokens select -- the query positions' own block always -- can come
-// from that XCD's L2 (128K spec-verify: 439.7 against 443.3 MB fetched per
-// step). Groups of 8 (sequence, KV head) pairs take 8 * q_len positions;
-// the pairs past the last full group keep their tokens adjacent.
+// Fused shape: the item (token * Hkv + g) at dispatch position r. The
+// q_len * Hkv items of one sequence sit 8 positions apart, so that they run
+// on one XCD (workgroups go to the 8 XCDs in turn): the blocks several of
+// its tokens select -- the query positions' own block always -- and the
+// tokens' tagged scores, read by every KV head, can come from that XCD's L2
+// (128K spec-verify: 436.3 against 443.3 MB fetched and 74.4-74.7 against
+// 75.7-76.1 us per step). Groups of 8 sequences take 8 * q_len * Hkv
+// positions; the sequences past the last full group keep their order.
 __device__ __forceinline__ int fused_item_at(const AttnArgs& a, int r) {
-  const int Tq = a.Tq, Hkv = a.Hkv, full = (a.B * Hkv / 8) * 8;
-  int pair, t;
-  if (r < full * Tq) {
-    const int grp = r / (8 * Tq), rem = r - grp * 8 * Tq;
-    t = rem / 8;
-    pair = 8 * grp + rem % 8;
-  } else {
-    const int r2 = r - full * Tq;
-    pair = full + r2 / Tq;
-    t = r2 % Tq;
-  }
-  return ((pair / Hkv) * Tq + t) * Hkv + pair % Hkv;
+  const int nit = a.Tq * a.Hkv, full = (a.B / 8) * 8;
+  if (r >= full * nit) return r;
+  const int grp = r / (8 * nit), rem = r - grp * 8 * nit;
+  return (8 * grp + rem % 8) * nit + rem / 8;
 }
 
 // ---------------------------------------------------------------- fused shape

@@ -37,8 +37,9 @@
 //                  ceil(count / S)), one block per wave. Splits s < S-1
 //                  publish their merged softmax state (m, l, O of every head
 //                  of the group) as tagged words; the last split's waves read
-//                  them in parallel and wave 0 merges splits 0, 1, ..., S-1
-//                  in that order, so the result does not depend on timing.
+//                  them in parallel, and each of its waves merges two of the
+//                  eight dim tiles of splits 0, 1, ..., S-1 in that order, so
+//                  the result does not depend on timing.
 // Every wait is on a workgroup earlier in dispatch order, and the indexer
 // workgroups wait on nothing: with each XCD dispatching its workgroups in
 // order, the earliest unfinished workgroup of the grid can always run to its

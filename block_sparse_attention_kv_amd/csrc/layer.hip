@@ -119,8 +119,18 @@ __device__ __forceinline__ int query_pos(const AttnArgs& a, int tok) {
   return clamp_ctx(a.ctx_lens[tok / a.Tq], a.maxb) - a.Tq + tok % a.Tq;
 }
 
-// Q^T operand, the attention of the W waves over the LDS block lists and
-// the merge of the wave states; wave 0 ends with the workgroup's state.
+// The attention of the W waves over the LDS block lists, given the Q^T
+// operand, and the merge of the wave states; wave 0 ends with the
+// workgroup's state.
+template <int MAXB>
+__device__ __forceinline__ void attend_q(const AttnArgs& a, int g, int p, const MfmaT<true>::vec (&qb)[4],
+                                         float cscale, const int32_t* blist, const int32_t* plist, int n,
+                                         uint8_t* lds, int wave, int lane, SoftmaxState& st) {
+  init_state(st);
+  stream_blocks<true, kLayerWaves, MAXB>(a, g, p, blist, plist, n, qb, cscale, lds, wave, lane, st);
+  merge_waves<kLayerWaves>(st, lds, wave, lane);
+}
+// The same from the raw bf16 queries.
 template <int MAXB>
 __device__ __forceinline__ void attend_list(const AttnArgs& a, int tok, int g, int p, const u32x4 (&qraw)[4],
                                             const int32_t* blist, const int32_t* plist, int n, uint8_t* lds,
@@ -128,9 +138,7 @@ __device__ __forceinline__ void attend_list(const AttnArgs& a, int tok, int g, i
   MfmaT<true>::vec qb[4];
   float cscale;
   convert_q<true>(a, qraw, qb, cscale);
-  init_state(st);
-  stream_blocks<true, kLayerWaves, MAXB>(a, g, p, blist, plist, n, qb, cscale, lds, wave, lane, st);
-  merge_waves<kLayerWaves>(st, lds, wave, lane);
+  attend_q<MAXB>(a, g, p, qb, cscale, blist, plist, n, lds, wave, lane, st);
 }
 
 // Leaves the top wave priority once the blocks are known: the later half of
@@ -316,8 +324,15 @@ __device__ void split_item(const LayerArgs& L, int tok, int g, int split, uint8_
   const int p = query_pos(a, tok);
   const uint64_t tag = (uint64_t)a.epoch << 32;
 
-  u32x4 qraw[4];
-  load_q(a, tok, g, lane, qraw);  // issued first: it does not depend on the selection
+  // Q^T operand first: it does not depend on the selection, and the
+  // conversion then overlaps the wait for the candidate records
+  MfmaT<true>::vec qb[4];
+  float cscale;
+  {
+    u32x4 qraw[4];
+    load_q(a, tok, g, lane, qraw);
+    convert_q<true>(a, qraw, qb, cscale);
+  }
 
   // ---- the token's candidate records -> the top-k blocks -> this split's share
   if (wave == 0) {
@@ -454,7 +469,7 @@ __device__ void split_item(const LayerArgs& L, int tok, int g, int split, uint8_
   }
   drop_priority(a, item);
   SoftmaxState st;
-  attend_list<MAXB>(a, tok, g, p, qraw, blist, plist, __builtin_amdgcn_readfirstlane(nlist), lds, wave, lane, st);
+  attend_q<MAXB>(a, g, p, qb, cscale, blist, plist, __builtin_amdgcn_readfirstlane(nlist), lds, wave, lane, st);
   if (S == 1) {
     if (wave == 0) write_out(a, tok, g, st, lane);
     return;

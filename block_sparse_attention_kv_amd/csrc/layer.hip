@@ -573,13 +573,22 @@ template <int KF, int HP, int TQ, int MAXB>
 __global__ __launch_bounds__(kLayerThreads, kLayerWgsPerCu) void decode_layer_single_kernel(LayerArgs L) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   if ((int)blockIdx.x < L.idx_wgs) {
-    // Split shape: the scan's end is the critical path. The second indexer
-    // workgroup of each compute unit (the later-dispatched half) loses issue
-    // arbitration to the older one and ends last; one priority step evens
-    // them out (512K: 40.4 against 40.7 us per step). In the fused shape the
-    // early end of the first half starts half of the items early, which pays
-    // more.
-    if (L.nsub > 0 && 2 * (int)blockIdx.x >= L.idx_wgs) __builtin_amdgcn_s_setprio(1);
+    // Wave priorities of the scan. Split shape: the scan's end is the
+    // critical path; the second indexer workgroup of each compute unit (the
+    // later-dispatched half) loses issue arbitration to the older one and
+    // ends last, and one priority step evens them out (512K: 40.4 against
+    // 40.7 us per step). Fused shape: the scan goes one step above the
+    // attention items that start in the slots of retired indexer workgroups
+    // (after their selection they run at 0 or 1), so that they do not hold
+    // back the scan that the later items wait for (ragged batch: 62.2
+    // against 66.4 us; 128K spec-verify unchanged). Evening out the two
+    // halves there instead delays the items that the early half's end
+    // lets start.
+    if (L.nsub > 0) {
+      if (2 * (int)blockIdx.x >= L.idx_wgs) __builtin_amdgcn_s_setprio(1);
+    } else {
+      __builtin_amdgcn_s_setprio(1);
+    }
     indexer_body<KF, HP, TQ, false, 2, true>(L.ia, reinterpret_cast<int32_t*>(lds), blockIdx.x, L.idx_wgs,
                                              L.aa.epoch);
     return;

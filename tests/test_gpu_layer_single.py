@@ -76,6 +76,17 @@ def test_single_more_items_than_grid():
     print("many items: ties %d, out max-abs %.2e mean-abs %.2e" % (ties, mx, mean))
 
 
+def test_single_more_than_four_selector_ranges():
+    # 4,098 to 8,192 blocks per context: 5 to 8 selector records per token in
+    # the split shape, so the attention workgroups hold the candidates in two
+    # slots per lane; the winners lie in every range
+    w = make_workload("single_8rec", 66, [8192 * 128, 6000 * 128 - 37, 4097 * 128 + 5], 1, 16, 1, 4, KV_NVFP4,
+                      IDX_FP8, table="permute", n_planted=6)
+    run = _same_as_two_kernel(w)
+    ties, mx, mean = G.layer_parity(w, run=run, single=True)
+    print("8 records: ties %d, out max-abs %.2e mean-abs %.2e" % (ties, mx, mean))
+
+
 def test_single_absent_pages():
     w = make_workload("single_absent", 64, [3000, 1200], 4, 16, 2, 8, KV_NVFP4, IDX_FP8, table="permute")
     w.block_table[0, 5] = -1

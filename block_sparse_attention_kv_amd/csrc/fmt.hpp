@@ -73,9 +73,17 @@ __device__ __forceinline__ uint32_t mul_f16x2(uint32_t a, uint32_t b) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
-// Broadcast the low / high fp16 of a packed pair into both halves.
-__device__ __forceinline__ uint32_t bcast_lo16(uint32_t x) { return __builtin_amdgcn_perm(x, x, 0x01000100u); }
-__device__ __forceinline__ uint32_t bcast_hi16(uint32_t x) { return __builtin_amdgcn_perm(x, x, 0x03020302u); }
+// Broadcast the low / high fp16 of a packed pair into both halves. Written
+// as a vector shuffle, so that a packed fp16 operation consuming it takes
+// the half through its operand-select bits instead of a separate permute.
+__device__ __forceinline__ uint32_t bcast_lo16(uint32_t x) {
+  const f16x2 v = __builtin_bit_cast(f16x2, x);
+  return __builtin_bit_cast(uint32_t, (f16x2)__builtin_shufflevector(v, v, 0, 0));
+}
+__device__ __forceinline__ uint32_t bcast_hi16(uint32_t x) {
+  const f16x2 v = __builtin_bit_cast(f16x2, x);
+  return __builtin_bit_cast(uint32_t, (f16x2)__builtin_shufflevector(v, v, 1, 1));
+}
 
 // Eight NVFP4 elements of one scale group: codes (dword) times the scale
 // given as a broadcast fp16 pair -> 8 fp16 (exact).

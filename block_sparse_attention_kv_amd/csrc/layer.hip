@@ -40,6 +40,9 @@
 //                  them in parallel, and each of its waves merges two of the
 //                  eight dim tiles of splits 0, 1, ..., S-1 in that order, so
 //                  the result does not depend on timing.
+// Contexts of at most 1,024 blocks get no selectors: every attention
+// workgroup then selects from the token's tagged pooled scores itself, as in
+// the fused shape, and the selector's hand-over is saved.
 // Every wait is on a workgroup earlier in dispatch order, and the indexer
 // workgroups wait on nothing: with each XCD dispatching its workgroups in
 // order, the earliest unfinished workgroup of the grid can always run to its
@@ -334,8 +337,48 @@ __device__ void split_item(const LayerArgs& L, int tok, int g, int split, uint8_
     convert_q<true>(a, qraw, qb, cscale);
   }
 
+  // ---- without selectors (contexts of at most one selector range): the
+  // workgroup selects from the token's tagged pooled scores itself, as in
+  // the fused shape, and takes its share of the blocks
+  if (L.nsub == 0) {
+    __shared__ TopkLds tk;
+    __shared__ int32_t sel_lds[kTopkMax];
+    const int nvis = p < 0 ? 0 : p / kBlock + 1;
+    int32_t* pages = reinterpret_cast<int32_t*>(lds);  // [nvis]
+    const int32_t* bt_row = a.block_table + (size_t)(tok / a.Tq) * a.maxb;
+    const TaggedScores tw{reinterpret_cast<const uint64_t*>(a.pooled) + (size_t)tok * a.maxb, a.epoch,
+                          a.spin_limit};
+    const int nsel = block_topk<kLayerThreads, true>([&](int i) { return 0.0f; },
+                                                     [&](int i) { return bt_row[i]; }, pages, nvis, a.top_k,
+                                                     a.keep_last != 0, sel_lds, tk, tw);
+    bool stale = false;
+#pragma unroll
+    for (int w = 0; w < kLayerWaves; w++) stale |= tk.stale[w] != 0;
+    if (wave == 0) {
+      // attended blocks (selected, page in range) in ascending order; this
+      // split takes positions [split * per, (split + 1) * per)
+      const int blk = lane < nsel ? sel_lds[lane] : -1;
+      const int page = lane < nsel ? pages[blk] : -1;
+      const bool ok = !stale && lane < nsel && page >= 0 && page < a.num_pages;
+      const uint64_t bal = __ballot(ok);
+      const int apos = __popcll(bal & ((1ull << lane) - 1ull));
+      const int cnt = __popcll(bal);
+      const int per = (cnt + S - 1) / S, first = split * per;
+      if (ok && apos >= first && apos < first + per) {
+        blist[apos - first] = blk;
+        plist[apos - first] = page;
+      }
+      if (split == 0 && g == 0 && a.sel && lane < a.top_k)
+        a.sel[(size_t)tok * a.top_k + lane] = (!stale && lane < nsel) ? blk : -1;
+      if (lane == 0) {
+        nlist = stale ? 0 : max(0, min(per, cnt - first));
+        bad = stale ? 1 : 0;
+        if (stale) report_give_up(L);
+      }
+    }
+  }
   // ---- the token's candidate records -> the top-k blocks -> this split's share
-  if (wave == 0) {
+  else if (wave == 0) {
     // candidate c = 16 r + e (record r, entry e) belongs to lane c % 64,
     // slot c / 64 (a second slot only with more than 4 records); the lane
     // reads the record's header and the entry's key, block and page words
@@ -584,7 +627,7 @@ __global__ __launch_bounds__(kLayerThreads, kLayerWgsPerCu) void decode_layer_si
     // against 66.4 us; 128K spec-verify unchanged). Evening out the two
     // halves there instead delays the items that the early half's end
     // lets start.
-    if (L.nsub > 0) {
+    if (L.nsub > 0 || L.aa.splits > 1) {
       if (2 * (int)blockIdx.x >= L.idx_wgs) __builtin_amdgcn_s_setprio(1);
     } else {
       __builtin_amdgcn_s_setprio(1);
@@ -594,7 +637,7 @@ __global__ __launch_bounds__(kLayerThreads, kLayerWgsPerCu) void decode_layer_si
     return;
   }
   const int r = (int)blockIdx.x - L.idx_wgs;
-  if (L.nsub == 0) {
+  if (L.nsub == 0 && L.aa.splits == 1) {
     // In the fused shape an item runs at the highest wave priority until it
     // knows its blocks: reading the tagged scores and selecting are a chain
     // of dependent steps with little issue work, on the critical path of
@@ -653,7 +696,9 @@ hipError_t launch_layer_single(const IndexerArgs& ia, const AttnArgs& aa, const 
   if (aa.top_k < 1 || aa.top_k > kTopkMax || aa.maxb < 1 || aa.maxb > kSelectMaxBlocks) return hipErrorInvalidValue;
   if (aa.B != ia.B || aa.Tq != ia.Tq || aa.maxb != ia.maxb || aa.ctx_lens != ia.ctx_lens) return hipErrorInvalidValue;
   if (aa.grp > 16 || aa.Tq < 1 || aa.Tq > 4) return hipErrorInvalidValue;
-  const int nsub = fused ? 0 : layer_selectors(aa.maxb);
+  // selectors only where a context spans more than one selector range; below
+  // that every split item selects from the pooled scores itself
+  const int nsub = (fused || aa.maxb <= kSubBlocks) ? 0 : layer_selectors(aa.maxb);
   if (nsub * kRecordWords > 7 * 64 || nsub * kTopkMax > 128) return hipErrorInvalidValue;
   const int64_t tokens = (int64_t)aa.B * aa.Tq;
   const int64_t work = fused ? tokens * aa.Hkv : tokens * (nsub + (int64_t)aa.Hkv * aa.splits);

@@ -189,8 +189,8 @@ def test_single_traced_matches_plain():
     assert np.array_equal(sel.cpu().numpy(), want["sel"])
 
 
-@pytest.mark.parametrize("shape", [0, 1])
-def test_single_bounded_wait_gives_up_cleanly(shape):
+@pytest.mark.parametrize("shape,ctx,nseq", [(0, 20000, 24), (1, 20000, 24), (0, 140000, 6)])
+def test_single_bounded_wait_gives_up_cleanly(shape, ctx, nseq):
     # With a poll limit of 1 a workgroup that finds the data it waits for
     # unpublished at the first poll gives up at once: the kernel still ends,
     # every (token, KV head) item is either the normal result or marked
@@ -199,7 +199,9 @@ def test_single_bounded_wait_gives_up_cleanly(shape):
     # query counts the workgroups
     # that stopped, and the default limit restores the normal result (and a
     # zero count) on the next call.
-    w = make_workload("single_spin", 69, [20000] * 24, 4, 16, 2, 8, KV_NVFP4, IDX_FP8, table="permute")
+    # shapes: split items selecting themselves (contexts of at most 1,024
+    # blocks), fused, and split items reading selector records (1,094 blocks)
+    w = make_workload("single_spin", 69, [ctx] * nseq, 4, 16, 2, 8, KV_NVFP4, IDX_FP8, table="permute")
     run = G.Run(w)
     prm = w.params
     B, Tq, Hkv, grp = prm["num_seqs"], prm["q_len"], prm["num_kv_heads"], prm["num_q_heads"] // prm["num_kv_heads"]
@@ -214,7 +216,7 @@ def test_single_bounded_wait_gives_up_cleanly(shape):
         torch.cuda.synchronize()
         return out.cpu().numpy(), lse.cpu().numpy(), sel.cpu().numpy()
 
-    msa.msa_debug_layer_splits(shape)  # 0: the automatic shape (split, for these 192 items); 1: fused
+    msa.msa_debug_layer_splits(shape)  # 0: the automatic shape (split, for these few items); 1: fused
     try:
         want = call()
         assert msa.msa_decode_layer_gave_up(run.params, ws) == 0

@@ -244,11 +244,13 @@ msa_status_t msa_decode_layer_traced(const msa_params_t* p, const msa_cache_t* c
  * pooling phase, which publishes every pooled score tagged with the call's
  * epoch, then the selection and attention. With at least one (sequence,
  * token, KV head) item per compute unit, one workgroup per item reads its
- * token's tagged scores, selects and attends. With fewer items, each token
- * gets selector workgroups (one per 1,024 blocks of max_blocks_per_seq)
- * that publish their top-k candidates as tagged records, and each item is
- * split over 4 attention workgroups that merge the candidates, attend to a
- * share of the selected blocks and meet through tagged partial softmax
+ * token's tagged scores, selects and attends. With fewer items, each item
+ * is split over 4 attention workgroups; where max_blocks_per_seq exceeds
+ * 1,024, each token first gets selector workgroups (one per 1,024 blocks)
+ * that publish their top-k candidates as tagged records for the attention
+ * workgroups to merge, otherwise each attention workgroup selects itself.
+ * The 4 workgroups of an item attend to a share of the selected blocks each
+ * and meet through tagged partial softmax
  * states, the last one merging them in a fixed order, so results do not
  * depend on timing. Same arguments, workspace and selection as
  * msa_decode_layer; out and lse equal msa_decode_layer's bit for bit from

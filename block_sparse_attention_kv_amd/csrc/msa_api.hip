@@ -222,10 +222,11 @@ bool recalled_epoch(const void* ws, uint32_t* e) {
 // item per compute unit, one workgroup per item selects and attends (fused).
 // With fewer items a lone item per compute unit streaming four blocks per
 // wave (and, over thousands of blocks, a selection by one workgroup) leaves
-// the chip idle: per token, selectors over 1,024-block ranges, and each item
-// split over 4 workgroups of one block per wave (32K-token contexts, 16
-// items: 22.6 against 23.9 us per step fused). A debug export can force the
-// shape: 1 = fused, 2 or 4 = split with that many workgroups per item.
+// the chip idle: each item split over 4 workgroups of one block per wave,
+// with selectors over 1,024-block ranges per token where a context spans
+// more than one range (32K-token contexts, 16 items: 20.3 against 23.9 us
+// per step fused). A debug export can force the shape: 1 = fused, 2 or 4 =
+// split with that many workgroups per item.
 std::atomic<int> g_layer_splits{0};
 int device_cus();
 int layer_splits(const msa_params_t* p) {

@@ -108,13 +108,17 @@ __device__ __forceinline__ void load_v(const KvRsrc& r, const LaneOff& o, VRegs&
 // ---------------------------------------------------------------- pieces
 
 // Raw Q^T operand of this lane: head g*grp + lane%16 of row bt, dims
-// 32*(lane/16) + 8s + e; zero for lanes past the group's heads.
+// 32*(lane/16) + 8s + e; zero for lanes past the group's heads. The group's
+// rows are one buffer range and those lanes read past its end (zeros), so
+// the loads take no branch: a branch around them made the compiler wait for
+// them at its join, before the selection's first reads were issued.
 __device__ __forceinline__ void load_q(const AttnArgs& a, int bt, int g, int lane, u32x4 (&qraw)[4]) {
   const int h = lane & 15, q4 = lane >> 4;
-  const bool ok = h < a.grp;
-  const uint16_t* qrow = a.q + ((size_t)bt * a.Hq + g * a.grp + h) * kHeadDim + 32 * q4;
+  const __amdgpu_buffer_rsrc_t r =
+      make_rsrc(a.q + ((size_t)bt * a.Hq + (size_t)g * a.grp) * kHeadDim, (uint32_t)(a.grp * kHeadDim * 2));
+  const uint32_t off = (uint32_t)(h * kHeadDim * 2 + 64 * q4);
 #pragma unroll
-  for (int s = 0; s < 4; s++) qraw[s] = ok ? reinterpret_cast<const u32x4*>(qrow)[s] : u32x4{0, 0, 0, 0};
+  for (int s = 0; s < 4; s++) qraw[s] = buf_load16<0>(r, off + 16 * s, 0);
 }
 
 // Q^T operand in the matrix-core format and the score scale (log2 domain,

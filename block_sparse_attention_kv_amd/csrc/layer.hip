@@ -117,9 +117,15 @@ __device__ void report_give_up(const LayerArgs& L) {
   }
 }
 
-// Last visible key of query token `tok` (sequence tok / Tq).
+// Last visible key of query token `tok` (sequence tok / Tq). The context
+// length is read through the scalar cache (the constant address space: the
+// array does not change during the call), so that the wait for it is not a
+// wait for every vector load issued before it; under the scan's memory load
+// each vector round trip costs microseconds.
 __device__ __forceinline__ int query_pos(const AttnArgs& a, int tok) {
-  return clamp_ctx(a.ctx_lens[tok / a.Tq], a.maxb) - a.Tq + tok % a.Tq;
+  typedef __attribute__((address_space(4))) const int32_t cint32;
+  const int32_t len = *reinterpret_cast<cint32*>(reinterpret_cast<uintptr_t>(a.ctx_lens + tok / a.Tq));
+  return clamp_ctx(len, a.maxb) - a.Tq + tok % a.Tq;
 }
 
 // The attention of the W waves over the LDS block lists, given the Q^T

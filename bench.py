@@ -31,9 +31,10 @@ Prints one JSON line on stdout (details on stderr):
   step         the step's algorithmic bytes term by term, rate and fraction
   cpu_baseline the float64 oracle on a bounded sample of the same workload,
                timed on this host's cores, and its comparison with the GPU
-  other_workloads  (default run) the 32K, 512K and ragged decode workloads:
-               step time, rate, fraction, and every query token's selection
-               checked against the oracle
+  other_workloads  (default run) the 32K, 512K and ragged decode workloads
+               and the 128K one with NVFP4 indexer keys: step time, rate,
+               fraction, and every query token's selection checked against
+               the oracle
 """
 import argparse
 import hashlib
@@ -394,14 +395,15 @@ def step_report(w, ms_step, sel):
     return terms, step_b, gbps
 
 
-def other_workload(cfg, steps, warmup, layer):
-    """Compact measurement of another decode workload: step time, rate,
-    fraction of the HBM peak, and the selection of every query token checked
-    against the oracle (tie-band and other differences counted)."""
+def other_workload(cfg, steps, warmup, layer, nvfp4_idx=False):
+    """Compact measurement of another decode workload (with nvfp4_idx, the
+    same configuration with NVFP4 indexer keys): step time, rate, fraction of
+    the HBM peak, and the selection of every query token checked against the
+    oracle (tie-band and other differences counted)."""
     from oracle import msa_oracle as O
-    from workloads import make_config, CONFIG_NAMES
+    from workloads import make_config, CONFIG_NAMES, IDX_NVFP4
     t0 = time.perf_counter()
-    w = make_config(cfg)
+    w = make_config(cfg, idx_dtype=IDX_NVFP4 if nvfp4_idx else None)
     run = Runner(w, layer)
     for i in range(warmup):
         run.step(i)
@@ -414,7 +416,9 @@ def other_workload(cfg, steps, warmup, layer):
     for b in range(w.B):
         compare_tokens(w, b, O.decode_sequence(w, b), gpu_res, acc)
     prm = w.params
-    rep = {"config_id": str(cfg), "workload": CONFIG_NAMES[cfg], "entry": entry, "steps": steps,
+    rep = {"config_id": str(cfg) + ("/nvfp4" if nvfp4_idx else ""),
+           "workload": CONFIG_NAMES[cfg] + (", NVFP4 idx keys instead of FP8" if nvfp4_idx else ""),
+           "entry": entry, "steps": steps,
            "warmup": warmup, "ms_per_step": ms, "tokens_per_s": prm["num_seqs"] * prm["q_len"] / (ms * 1e-3),
            "algorithmic_bytes": step_b, "gbps": gbps, "frac": gbps / HBM_PEAK_GBPS,
            "oracle_check": acc_summary(acc)}
@@ -590,8 +594,8 @@ def main():
     if not args.no_others and args.config == 3 and args.idx_dtype == "fp8":
         # 300 untimed steps each (at most ~21 ms), so that these compact
         # measurements are of the steady state too
-        res["other_workloads"] = [other_workload(c, args.other_steps, max(args.warmup, 300), args.layer)
-                                  for c in (2, 4, 5)]
+        res["other_workloads"] = [other_workload(c, args.other_steps, max(args.warmup, 300), args.layer, nv)
+                                  for c, nv in ((2, False), (4, False), (5, False), (3, True))]
     print(json.dumps(res), flush=True)
 
 

@@ -77,12 +77,14 @@ __device__ __forceinline__ KvRsrc nvfp4_rsrc(const AttnArgs& a, int page, int g,
 }
 
 // This lane's share of a block: K codes of key kappa(tau, l%16), dims
-// 32*(l/16) .. +31 (16 bytes), and the two E4M3 scales of those dims; V codes
-// of dim 16*dt + l%16, tokens 32*(l/16) .. +31, and 16 bytes of the [8][128]
-// V scale array.
+// 32*(l/16) .. +31 (16 bytes), and 16 bytes of the [128][8] K scale array
+// (the scales a lane uses lie 32 bytes apart: the wave loads the whole array
+// with one instruction and exchanges it through LDS, where eight 2-byte loads
+// per block cost more vector memory issue); V codes of dim 16*dt + l%16,
+// tokens 32*(l/16) .. +31, and 16 bytes of the [8][128] V scale array.
 struct KRegs {
   u32x4 kd[8];
-  uint32_t ks[8];
+  u32x4 ks;
 };
 struct VRegs {
   u32x4 vd[8];
@@ -96,8 +98,8 @@ __device__ __forceinline__ void load_k(const KvRsrc& r, const LaneOff& o, KRegs&
 #pragma unroll
   for (int tau = 0; tau < 8; tau++) {
     K.kd[tau] = buf_load16<kAuxNT>(r.kd, o.k, (uint32_t)(64 * ktau(tau)));
-    K.ks[tau] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r.ks, (int)o.ks, 8 * ktau(tau), kAuxNT);
   }
+  K.ks = buf_load16<kAuxNT>(r.ks, o.ks, 0);
 }
 __device__ __forceinline__ void load_v(const KvRsrc& r, const LaneOff& o, VRegs& V) {
 #pragma unroll
@@ -176,7 +178,7 @@ __device__ __forceinline__ void init_state(SoftmaxState& st) {
 // This wave's online softmax and P.V over blocks wave, wave + W, ... < n of
 // the lists blist (logical block) / plist (page) in LDS; at most MAXB blocks
 // per wave. p: the query's last visible key. Ends with st.l summed over the
-// four lanes of each head. lds: at least W * 2 KB (V-scale stages).
+// four lanes of each head. lds: at least W * 4 KB (K- and V-scale stages).
 template <bool NVFP4, int W, int MAXB>
 __device__ __forceinline__ void stream_blocks(const AttnArgs& a, int g, int p, const int32_t* blist,
                                               const int32_t* plist, int n,
@@ -251,12 +253,14 @@ __device__ __forceinline__ void stream_blocks(const AttnArgs& a, int g, int p, c
   };
 
   if constexpr (NVFP4) {
-    // fp16 V scales of the current block: [8 groups][128 keys] per wave
+    // fp16 V scales of the current block: [8 groups][128 keys] per wave; fp16
+    // K scales: [128 keys][8 groups] per wave
     f16* vs_stage = reinterpret_cast<f16*>(lds) + wave * 1024;
+    f16* ks_stage = reinterpret_cast<f16*>(lds) + (W + wave) * 1024;
     const int rho = lane & 15;
     LaneOff off;
     off.k = (uint32_t)((32 * (rho >> 2) + (rho & 3)) * 64 + 16 * q4);
-    off.ks = (uint32_t)((32 * (rho >> 2) + (rho & 3)) * 8 + 2 * q4);
+    off.ks = (uint32_t)(16 * lane);
     off.v = (uint32_t)(rho * 64 + 16 * q4);
     off.vs = (uint32_t)(16 * lane);
     KRegs K;
@@ -282,11 +286,21 @@ __device__ __forceinline__ void stream_blocks(const AttnArgs& a, int g, int p, c
       const int pgn = none ? 0 : __builtin_amdgcn_readfirstlane(plist[i + W]);
       const KvRsrc rn = nvfp4_rsrc(a, pgn, g, none);
 
+      // ---- K scales to fp16 in LDS (wave-private; the previous block's
+      // reads of the stage are done: LDS operations of a wave stay in order)
+      {
+        u32x4* dst = reinterpret_cast<u32x4*>(ks_stage + 16 * lane);
+        dst[0] = fp8x8_f16(K.ks.x, K.ks.y);
+        dst[1] = fp8x8_f16(K.ks.z, K.ks.w);
+        wave_lds_sync();
+      }
+
       // ---- S^T = K Q^T, then the next block's K
       f32x4 sacc[8];
 #pragma unroll
       for (int tau = 0; tau < 8; tau++) {
-        const uint32_t sc2 = fp8x2_f16x2<false>(K.ks[tau]);  // groups 2*q4, 2*q4+1
+        // groups 2*q4, 2*q4+1 of key kappa(tau, rho)
+        const uint32_t sc2 = *reinterpret_cast<const uint32_t*>(ks_stage + 8 * kappa(tau, rho) + 2 * q4);
         const uint32_t slo = bcast_lo16(sc2), shi = bcast_hi16(sc2);
         f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -593,10 +607,10 @@ __device__ __forceinline__ void attn_body(const AttnArgs& a, int wg, uint8_t* ld
 }
 
 // Dynamic LDS: the pooled scores of one token (fused selection), the
-// per-wave V-scale stages, and the merge slots reuse one region.
+// per-wave K- and V-scale stages, and the merge slots reuse one region.
 inline size_t attn_lds_bytes(const AttnArgs& a, int W) {
   size_t sel = a.pooled ? (size_t)a.maxb * sizeof(int32_t) : 0;  // page table
-  size_t stage = (size_t)W * 1024 * 2;
+  size_t stage = (size_t)W * 1024 * 4;
   size_t merge = (size_t)(W / 2) * kSlotFloats * 4;
   size_t m = sel > stage ? sel : stage;
   return m > merge ? m : merge;

@@ -724,11 +724,11 @@ hipError_t launch_layer_single(const IndexerArgs& ia, const AttnArgs& aa, const 
   }
   if (!kern) return hipErrorInvalidValue;
   // dynamic LDS: the indexer's prefix sums, the selection's page table, the
-  // attention's V-scale stages, wave-merge slots and split states share one
+  // attention's K- and V-scale stages, wave-merge slots and split states share one
   // region
   size_t lds = ((size_t)ia.B + 1) * sizeof(int32_t);
   const size_t pages = (size_t)aa.maxb * sizeof(int32_t);
-  const size_t stage = (size_t)kLayerWaves * 1024 * 2;
+  const size_t stage = (size_t)kLayerWaves * 1024 * 4;
   const size_t merge = (size_t)kLayerWaves * kSlotFloats * 4;  // the last split's S <= 4 states
   lds = lds > pages ? lds : pages;
   lds = lds > stage ? lds : stage;

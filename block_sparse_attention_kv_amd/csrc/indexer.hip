@@ -58,7 +58,7 @@ namespace {
 
 template <int KF, int HP, int TQ, bool SCORES>
 __global__ __launch_bounds__(256, indexer_occupancy(KF, HP, TQ)) void indexer_pool_kernel(IndexerArgs a) {
-  extern __shared__ int32_t prefix[];  // [B + 1]: first work block of each sequence
+  extern __shared__ __attribute__((aligned(16))) int32_t prefix[];  // indexer_lds_bytes(B): prefix sums, scale stages
   indexer_body<KF, HP, TQ, SCORES, 1>(a, prefix, blockIdx.x, gridDim.x);
 }
 
@@ -78,7 +78,7 @@ int persistent_grid(const IndexerArgs& a, int occupancy, size_t lds) {
 
 template <int KF, int HP, bool SCORES>
 hipError_t launch_hp(const IndexerArgs& a, hipStream_t s, const KTimer* tm) {
-  const size_t lds = ((size_t)a.B + 1) * sizeof(int32_t);
+  const size_t lds = indexer_lds_bytes(a.B);
   switch (a.Tq) {
 #define MSA_TQ_CASE(T)                                                                                 \
   case T:                                                                                              \

@@ -24,7 +24,8 @@ constexpr int kKfBf16 = 0, kKfFp8 = 1, kKfNvfp4 = 2;
 constexpr uint32_t key_row_bytes(int kf) { return kf == kKfBf16 ? 128u : kf == kKfFp8 ? 64u : 32u; }
 
 // This lane's share of one tile (16 keys x 64 dims): key 16k + l%16,
-// dims 16*(l/16) .. 16*(l/16) + 15.
+// dims 16*(l/16) .. 16*(l/16) + 15. NVFP4 keys' scales come per block
+// (load_kscales).
 template <int KF>
 struct KTile;
 template <>
@@ -39,7 +40,6 @@ struct KTile<kKfBf16> {
 template <>
 struct KTile<kKfNvfp4> {
   u32x2 c;     // 16 E2M1 codes
-  uint32_t s;  // the group's E4M3 scale (low byte)
 };
 
 // Lane offset (bytes) of this lane's share of tile 0 inside a page; tile k
@@ -78,12 +78,31 @@ __device__ __forceinline__ void load_ktile(const PageRsrc<KF>& r, int k, int lan
     t.s = buf_load4f<kIdxAux>(r.scales, (uint32_t)(4 * (lane & 15)), (uint32_t)(64 * k));
   } else if constexpr (KF == kKfNvfp4) {
     t.c = buf_load8<kIdxAux>(r.keys, voff, soff);
-    t.s = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r.scales, 4 * (lane & 15) + (lane >> 4), 64 * k, kIdxAux);
   } else {
     t.v[0] = buf_load16<kIdxAux>(r.keys, voff, soff);
     t.v[1] = buf_load16<kIdxAux>(r.keys, voff + 16, soff);
   }
 }
+
+// NVFP4 keys: the four E4M3 group scales of every key of a block (512
+// bytes); lane l holds keys 2l and 2l+1. A lane uses one scale byte of a
+// different key in every tile, so the wave loads the block's scales with one
+// instruction and exchanges them through LDS (score_block): eight 1-byte
+// loads per block cost more vector memory issue than the exchange (128K with
+// NVFP4 keys: 61.8-62.0 against 62.2-62.9 us). FP8 keys keep one 4-byte
+// load per tile, which ran faster than the exchange (128K: 72.1-72.5 against
+// 73.2-73.4 us).
+template <int KF>
+__device__ __forceinline__ u32x2 load_kscales(const PageRsrc<KF>& r, int lane) {
+  if constexpr (KF != kKfNvfp4) return u32x2{0u, 0u};
+  else return buf_load8<kIdxAux>(r.scales, (uint32_t)(8 * lane), 0u);
+}
+constexpr uint32_t kScaleStageBytes = kBlock * 4;  // per wave
+
+// Dynamic LDS of the scan: the prefix sums (B + 1 ints), then four waves'
+// scale stages.
+__host__ __device__ constexpr size_t indexer_stage_offset(int B) { return (((size_t)B + 1) * 4 + 15) & ~(size_t)15; }
+__host__ __device__ constexpr size_t indexer_lds_bytes(int B) { return indexer_stage_offset(B) + 4 * kScaleStageBytes; }
 
 // DPP lane moves (gfx9 encodings): quad_perm and row_ror.
 template <int CTRL>
@@ -191,17 +210,26 @@ __device__ __forceinline__ void load_seq(const IndexerArgs& a, int b, int Lc, in
   }
 }
 
-// Scores of one block held in the ring T (8 tiles of 16 keys); refills the
-// ring with the next block when PREFETCH. mx[tau]: this lane's max over its
-// keys for token 4*tau + g.
+// Scores of one block held in the ring T (8 tiles of 16 keys) and, for NVFP4
+// keys, its scales ks_blk; refills both with the next block when PREFETCH.
+// stage: this wave's kScaleStageBytes of LDS. mx[tau]: this lane's max over its keys for
+// token 4*tau + g.
 template <int KF, int HP, int TQ, bool PREFETCH, bool SCORES>
-__device__ __forceinline__ void score_block(const IndexerArgs& a, KTile<KF> (&T)[8], const SeqState<KF, HP, TQ>& st,
-                                            int b, int lane, uint32_t loff, int blk, bool absent,
-                                            const PageRsrc<KF>& rn, float (&mx)[Shape<HP, TQ>::NTT]) {
+__device__ __forceinline__ void score_block(const IndexerArgs& a, KTile<KF> (&T)[8], u32x2& ks_blk, uint8_t* stage,
+                                            const SeqState<KF, HP, TQ>& st, int b, int lane, uint32_t loff, int blk,
+                                            bool absent, const PageRsrc<KF>& rn, float (&mx)[Shape<HP, TQ>::NTT]) {
   typedef Shape<HP, TQ> S;
   const int g = lane >> 4;
 #pragma unroll
   for (int tau = 0; tau < S::NTT; tau++) mx[tau] = -INFINITY;
+  // NVFP4: the block's scales to LDS (the previous block's reads of the
+  // stage are done: LDS operations of a wave stay in order), then the next
+  // block's
+  if constexpr (KF == kKfNvfp4) {
+    *reinterpret_cast<u32x2*>(stage + 8 * lane) = ks_blk;
+    wave_lds_sync();
+    if constexpr (PREFETCH) ks_blk = load_kscales<KF>(rn, lane);
+  }
 #pragma unroll
   for (int k = 0; k < 8; k++) {
     typedef typename KeyVec<KF>::type vec;
@@ -212,7 +240,8 @@ __device__ __forceinline__ void score_block(const IndexerArgs& a, KTile<KF> (&T)
       kb[1] = __builtin_bit_cast(vec, fp8x8_bf16(T[k].v.z, T[k].v.w));
       ks = T[k].s;
     } else if constexpr (KF == kKfNvfp4) {
-      const uint32_t s2 = bcast_lo16(fp8x2_f16x2<false>(T[k].s));
+      const uint32_t sraw = stage[4 * (16 * k + (lane & 15)) + g];  // the group's E4M3 scale
+      const uint32_t s2 = bcast_lo16(fp8x2_f16x2<false>(sraw));
       kb[0] = __builtin_bit_cast(vec, nvfp4x8_f16(T[k].c.x, s2));
       kb[1] = __builtin_bit_cast(vec, nvfp4x8_f16(T[k].c.y, s2));
       ks = a.idx_ts * st.kq;
@@ -269,8 +298,8 @@ constexpr int indexer_occupancy(int kf, int hp, int tq) {
 
 // The indexer scan of workgroup wg of nwg (persistent: every workgroup of the
 // grid calls it once). SCORES: write every key's score instead of the pooled
-// block maxima. NRING tile rings per wave (blocks in flight); prefix: LDS for
-// B + 1 ints. Wave w of the workgroup scans the global work blocks
+// block maxima. NRING tile rings per wave (blocks in flight); prefix: the
+// dynamic LDS, indexer_lds_bytes(B) bytes. Wave w of the workgroup scans the global work blocks
 // [W * total / (4 nwg), (W + 1) * total / (4 nwg)), W = 4 wg + w, where the
 // work blocks of the batch are numbered sequence after sequence.
 // COHERENT: for readers in the same grid, every pooled score is stored as
@@ -287,6 +316,8 @@ __device__ __forceinline__ void indexer_body(const IndexerArgs& a, int32_t* pref
   const int tid = threadIdx.x, lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps loop control scalar
   const uint32_t loff = ktile_lane_off<KF>(lane);
+  // this wave's scale stage, after the prefix sums
+  uint8_t* stage = reinterpret_cast<uint8_t*>(prefix) + indexer_stage_offset(a.B) + wave * kScaleStageBytes;
 
   // ---- prefix sum of work blocks over the batch (each thread: a run of
   // consecutive sequences)
@@ -351,11 +382,13 @@ __device__ __forceinline__ void indexer_body(const IndexerArgs& a, int32_t* pref
         const int pg = a.block_table[(size_t)b * a.maxb + w0 + lane];
         if (pg >= 0 && pg < a.num_pages) mypage = pg;
       }
-      // NRING rings: block i sits in ring i % NRING
+      // NRING rings: block i sits in ring i % NRING (codes T, scales KS)
       KTile<KF> T[NRING][8];
+      u32x2 KS[NRING];
       if constexpr (NRING == 1) {
         const int pg = __builtin_amdgcn_readfirstlane(mypage);
         const PageRsrc<KF> r0 = page_rsrc<KF>(a, pg, pg < 0);
+        KS[0] = load_kscales<KF>(r0, lane);
 #pragma unroll
         for (int k = 0; k < 8; k++) load_ktile<KF>(r0, k, lane, loff, T[0][k]);
       } else {
@@ -363,6 +396,7 @@ __device__ __forceinline__ void indexer_body(const IndexerArgs& a, int32_t* pref
         for (int r = 0; r < NRING; r++) {
           const int pg = r < nb ? __builtin_amdgcn_readlane(mypage, r) : -1;
           const PageRsrc<KF> r0 = page_rsrc<KF>(a, pg, pg < 0);
+          KS[r] = load_kscales<KF>(r0, lane);
 #pragma unroll
           for (int k = 0; k < 8; k++) load_ktile<KF>(r0, k, lane, loff, T[r][k]);
         }
@@ -396,11 +430,12 @@ __device__ __forceinline__ void indexer_body(const IndexerArgs& a, int32_t* pref
           const bool absent = __builtin_amdgcn_readlane(mypage, i) < 0;
           const int pgn = __builtin_amdgcn_readlane(mypage, i + 1);
           const PageRsrc<KF> rn = page_rsrc<KF>(a, pgn, pgn < 0);
-          score_block<KF, HP, TQ, true, SCORES>(a, T[0], st, b, lane, loff, w0 + i, absent, rn, mx);
+          score_block<KF, HP, TQ, true, SCORES>(a, T[0], KS[0], stage, st, b, lane, loff, w0 + i, absent, rn, mx);
           keep_max(i);
         }
         const bool absent = __builtin_amdgcn_readlane(mypage, i) < 0;
-        score_block<KF, HP, TQ, false, SCORES>(a, T[0], st, b, lane, loff, w0 + i, absent, PageRsrc<KF>{}, mx);
+        score_block<KF, HP, TQ, false, SCORES>(a, T[0], KS[0], stage, st, b, lane, loff, w0 + i, absent,
+                                               PageRsrc<KF>{}, mx);
         keep_max(i);
       } else {
       for (; i + NRING < nb; i += NRING) {
@@ -409,7 +444,8 @@ __device__ __forceinline__ void indexer_body(const IndexerArgs& a, int32_t* pref
           const bool absent = __builtin_amdgcn_readlane(mypage, i + r) < 0;
           const int pgn = i + r + NRING < nb ? __builtin_amdgcn_readlane(mypage, i + r + NRING) : -1;
           const PageRsrc<KF> rn = page_rsrc<KF>(a, pgn, pgn < 0);
-          score_block<KF, HP, TQ, true, SCORES>(a, T[r], st, b, lane, loff, w0 + i + r, absent, rn, mx);
+          score_block<KF, HP, TQ, true, SCORES>(a, T[r], KS[r], stage, st, b, lane, loff, w0 + i + r, absent, rn,
+                                                mx);
           keep_max(i + r);
         }
       }
@@ -417,8 +453,8 @@ __device__ __forceinline__ void indexer_body(const IndexerArgs& a, int32_t* pref
       for (int r = 0; r < NRING; r++) {
         if (i + r < nb) {
           const bool absent = __builtin_amdgcn_readlane(mypage, i + r) < 0;
-          score_block<KF, HP, TQ, false, SCORES>(a, T[r], st, b, lane, loff, w0 + i + r, absent, PageRsrc<KF>{},
-                                                 mx);
+          score_block<KF, HP, TQ, false, SCORES>(a, T[r], KS[r], stage, st, b, lane, loff, w0 + i + r, absent,
+                                                 PageRsrc<KF>{}, mx);
           keep_max(i + r);
         }
       }

@@ -723,10 +723,10 @@ hipError_t launch_layer_single(const IndexerArgs& ia, const AttnArgs& aa, const 
     case kKfNvfp4: kern = hp == 8 ? pick_tq<kKfNvfp4, 8>(aa.Tq, maxb) : pick_tq<kKfNvfp4, 4>(aa.Tq, maxb); break;
   }
   if (!kern) return hipErrorInvalidValue;
-  // dynamic LDS: the indexer's prefix sums, the selection's page table, the
+  // dynamic LDS: the indexer's prefix sums and scale stages, the selection's page table, the
   // attention's K- and V-scale stages, wave-merge slots and split states share one
   // region
-  size_t lds = ((size_t)ia.B + 1) * sizeof(int32_t);
+  size_t lds = indexer_lds_bytes(ia.B);
   const size_t pages = (size_t)aa.maxb * sizeof(int32_t);
   const size_t stage = (size_t)kLayerWaves * 1024 * 4;
   const size_t merge = (size_t)kLayerWaves * kSlotFloats * 4;  // the last split's S <= 4 states
